@@ -1,0 +1,137 @@
+"""Workload shapes and seeded synthetic inputs.
+
+This module only describes shapes and draws random numbers; it holds none of
+the attention arithmetic, so both the GPU path and the CPU oracle can be fed
+from it.
+
+Recipe (the same for every workload):
+  1. if the workload has ragged KV lengths, draw them first, on a CPU
+     torch.Generator seeded with `seed`: integers uniform on [lo, hi], both
+     ends included;
+  2. on a torch.Generator of the target device seeded with `seed`, draw Q,
+     then K, then V as float32 standard normals (`torch.randn`);
+  3. multiply K by the workload's `k_mult` (a power of two, so exact);
+  4. cast to the workload dtype (bf16 by round-to-nearest-even).
+Values therefore depend on the device the generator runs on; every check
+compares the GPU output against the oracle evaluated on the very tensors the
+GPU received.
+"""
+from dataclasses import dataclass, field
+import math
+
+import torch
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    kind: str            # "prefill" or "decode"
+    B: int
+    Hq: int
+    Hkv: int
+    Sq: int
+    Skv: int             # key/value length; for decode, the cache capacity
+    d: int
+    dtype: str           # "f32" or "bf16"
+    causal: bool
+    k_mult: float = 1.0
+    len_range: tuple = None   # (lo, hi) inclusive for ragged decode lengths
+    note: str = field(default="", compare=False)
+
+    @property
+    def scale(self):
+        return 1.0 / math.sqrt(self.d)
+
+    @property
+    def torch_dtype(self):
+        return torch.float32 if self.dtype == "f32" else torch.bfloat16
+
+    def describe(self):
+        s = (f"{self.kind} {self.dtype} B{self.B} Hq{self.Hq} Hkv{self.Hkv} "
+             f"Sq{self.Sq} Skv{self.Skv} d{self.d}")
+        if self.causal:
+            s += " causal"
+        if self.k_mult != 1.0:
+            s += f" Kx{self.k_mult:g}"
+        if self.len_range:
+            s += f" L~U[{self.len_range[0]},{self.len_range[1]}]"
+        return s
+
+
+WORKLOADS = [
+    Workload("prefill_f32_small", "prefill", 1, 2, 2, 128, 128, 64, "f32", True,
+             note="causal prefill, fp32, oracle-sized"),
+    Workload("prefill_bf16_b4h32s4096", "prefill", 4, 32, 32, 4096, 4096, 128, "bf16", True,
+             note="causal prefill, bf16 in / fp32 accumulate"),
+    Workload("decode_bf16_b64h32l4096", "decode", 64, 32, 32, 1, 4096, 128, "bf16", False,
+             note="single-query decode over a bf16 KV cache, every length 4096"),
+    Workload("decode_gqa_bf16_b128h32kv8", "decode", 128, 32, 8, 1, 8192, 128, "bf16", False,
+             len_range=(256, 8192), note="GQA decode, ragged lengths"),
+    Workload("prefill_gqa_bf16_h64kv8s16384", "prefill", 1, 64, 8, 16384, 16384, 128, "bf16",
+             True, k_mult=4.0, note="long causal GQA prefill, K scaled by 4"),
+]
+BY_NAME = {w.name: w for w in WORKLOADS}
+
+
+def kv_lengths(w, seed=0):
+    """Per-sequence KV lengths (int32, CPU) for workload w."""
+    if w.len_range is None:
+        return torch.full((w.B,), w.Skv, dtype=torch.int32)
+    g = torch.Generator(device="cpu").manual_seed(seed)
+    lo, hi = w.len_range
+    return torch.randint(lo, hi + 1, (w.B,), generator=g, dtype=torch.int64).to(torch.int32)
+
+
+def generate(w, device="cpu", seed=0):
+    """Seeded inputs for workload w on `device`.
+
+    Returns dict(q, k, v, kv_lens) with q [B,Hq,Sq,d], k/v [B,Hkv,Skv,d] in the
+    workload dtype and kv_lens int32 [B] (on `device`).
+    """
+    lens = kv_lengths(w, seed)
+    dev = torch.device(device)
+    g = torch.Generator(device=dev).manual_seed(seed)
+    q = torch.randn((w.B, w.Hq, w.Sq, w.d), generator=g, device=dev, dtype=torch.float32)
+    q = q.to(w.torch_dtype)
+    k = torch.randn((w.B, w.Hkv, w.Skv, w.d), generator=g, device=dev, dtype=torch.float32)
+    if w.k_mult != 1.0:
+        k.mul_(w.k_mult)
+    k = k.to(w.torch_dtype)
+    v = torch.randn((w.B, w.Hkv, w.Skv, w.d), generator=g, device=dev, dtype=torch.float32)
+    v = v.to(w.torch_dtype)
+    return {"q": q, "k": k, "v": v, "kv_lens": lens.to(dev)}
+
+
+def random_problem(B, Hq, Hkv, Sq, Skv, d, dtype="bf16", device="cpu", seed=0, k_mult=1.0,
+                   len_range=None):
+    """Seeded inputs of an arbitrary shape, drawn by the same recipe."""
+    w = Workload("adhoc", "prefill", B, Hq, Hkv, Sq, Skv, d, dtype, False, k_mult=k_mult,
+                 len_range=len_range)
+    return generate(w, device, seed)
+
+
+def prefill_flops(w, kv_lens=None):
+    """Algorithmic FLOPs of one call: 4*d per visible (query, key) pair.
+
+    Two multiply-adds per pair per feature: one for the score, one for P V.
+    Masked pairs are not counted.
+    """
+    lens = kv_lens if kv_lens is not None else torch.full((w.B,), w.Skv)
+    i = torch.arange(w.Sq, dtype=torch.int64)
+    pairs = 0
+    for b in range(w.B):
+        n = max(0, min(w.Skv, int(lens[b])))
+        if w.causal:
+            # query i sees keys j <= i + n - Sq with j < n
+            pairs += int((i + (n - w.Sq + 1)).clamp(0, n).sum())
+        else:
+            pairs += w.Sq * n
+    return 4 * w.d * w.Hq * pairs
+
+
+def decode_kv_bytes(w, kv_lens):
+    """Algorithmic K+V bytes of one decode call: every visible cache row of
+    every (batch, KV head) read once."""
+    elt = 4 if w.dtype == "f32" else 2
+    total = sum(max(0, min(w.Skv, int(x))) for x in kv_lens)
+    return 2 * total * w.Hkv * w.d * elt
