@@ -1,0 +1,204 @@
+"""Fused attention forward for MI355X (gfx950): Python binding of libattn.so.
+
+Thin ctypes layer over the C ABI in include/attn.h.  The functions named
+attn_* take raw device pointers and sizes and return the C status code,
+exactly like their C counterparts.  `prefill()` and `decode()` marshal torch
+tensors onto those calls: they check shapes, dtypes and devices, allocate the
+output, pass torch's current HIP stream and keep a per-device decode
+workspace.  Every step of the computation runs in the HIP kernels; there is
+no fallback path: the library is loaded on first use, and every entry point
+raises ImportError if libattn.so has not been built.
+"""
+import ctypes
+import math
+import os
+import threading
+
+import torch
+
+__all__ = [
+    "ATTN_F32", "ATTN_BF16", "AttnError", "attn_prefill_fwd", "attn_decode_fwd",
+    "attn_decode_workspace_bytes", "attn_status_str", "attn_last_hip_error", "prefill", "decode",
+    "library_path",
+]
+
+ATTN_F32 = 0
+ATTN_BF16 = 1
+STATUS = {0: "ATTN_OK", 1: "ATTN_ERR_NULL", 2: "ATTN_ERR_SHAPE", 3: "ATTN_ERR_UNSUPPORTED",
+          4: "ATTN_ERR_ALIGN", 5: "ATTN_ERR_WORKSPACE", 6: "ATTN_ERR_HIP", 7: "ATTN_ERR_VALUE"}
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+library_path = os.path.join(_HERE, "libattn.so")
+
+_lib = None
+_lock = threading.Lock()
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(library_path):
+            raise ImportError(
+                f"{library_path} is missing: build it with "
+                "`python -m attention_attn_fwd_11_amd.build` (hipcc, gfx950)")
+        # torch is imported first so the library binds to the HIP runtime torch loaded.
+        lib = ctypes.CDLL(library_path)
+        vp, i32, f32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
+        lib.attn_prefill_fwd.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, f32,
+                                         vp, ctypes.c_int, vp]
+        lib.attn_prefill_fwd.restype = ctypes.c_int
+        lib.attn_decode_fwd.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, f32,
+                                        vp, ctypes.c_int, vp, sz, vp]
+        lib.attn_decode_fwd.restype = ctypes.c_int
+        lib.attn_decode_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
+        lib.attn_decode_workspace_bytes.restype = sz
+        lib.attn_status_str.argtypes = [ctypes.c_int]
+        lib.attn_status_str.restype = ctypes.c_char_p
+        lib.attn_last_hip_error.argtypes = []
+        lib.attn_last_hip_error.restype = ctypes.c_char_p
+        _lib = lib
+    return _lib
+
+
+# ---------------------------------------------------------------------------
+# Same-name wrappers of the C ABI (raw pointers as Python ints, C status out).
+# ---------------------------------------------------------------------------
+def attn_prefill_fwd(q, k, v, o, B, H_q, H_kv, S_q, S_kv, d, causal, scale, kv_lens, dtype, stream):
+    return _load().attn_prefill_fwd(q, k, v, o, B, H_q, H_kv, S_q, S_kv, d, causal, scale, kv_lens,
+                                    dtype, stream)
+
+
+def attn_decode_fwd(q, k_cache, v_cache, o, B, H_q, H_kv, S_q, S_kv, d, causal, scale, kv_lens,
+                    dtype, workspace, workspace_bytes, stream):
+    return _load().attn_decode_fwd(q, k_cache, v_cache, o, B, H_q, H_kv, S_q, S_kv, d, causal,
+                                   scale, kv_lens, dtype, workspace, workspace_bytes, stream)
+
+
+def attn_decode_workspace_bytes(B, H_q, H_kv, S_kv, d):
+    return int(_load().attn_decode_workspace_bytes(B, H_q, H_kv, S_kv, d))
+
+
+def attn_status_str(status):
+    return _load().attn_status_str(status).decode()
+
+
+def attn_last_hip_error():
+    return _load().attn_last_hip_error().decode()
+
+
+class AttnError(RuntimeError):
+    def __init__(self, status, where):
+        self.status = status
+        msg = f"{where}: {STATUS.get(status, status)} ({attn_status_str(status)})"
+        if status == 6:
+            msg += f": {attn_last_hip_error()}"
+        super().__init__(msg)
+
+
+# ---------------------------------------------------------------------------
+# torch-facing helpers
+# ---------------------------------------------------------------------------
+_DTYPES = {torch.float32: ATTN_F32, torch.bfloat16: ATTN_BF16}
+_workspaces = {}
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _check_tensor(name, t, dtype=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a HIP device, got {t.device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+
+
+def _lens(kv_lens, B, device):
+    if kv_lens is None:
+        return None
+    _check_tensor("kv_lens", kv_lens, torch.int32)
+    if tuple(kv_lens.shape) != (B,) or kv_lens.device != device:
+        raise ValueError("kv_lens must be int32 [B] on the same device as q")
+    return kv_lens
+
+
+def prefill(q, k, v, causal=True, scale=None, kv_lens=None, out=None):
+    """Attention forward.  q [B,H_q,S_q,d]; k, v [B,H_kv,S_kv,d]; fp32 or bf16.
+
+    Returns o [B,H_q,S_q,d] with q's dtype.  kv_lens (optional) is int32 [B]
+    on the device.  Runs on torch's current stream for q's device.
+    """
+    if q.dtype not in _DTYPES:
+        raise TypeError(f"unsupported dtype {q.dtype}")
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _check_tensor(name, t, q.dtype)
+        if t.dim() != 4:
+            raise ValueError(f"{name} must be [B, H, S, d]")
+    B, H_q, S_q, d = q.shape
+    Bk, H_kv, S_kv, dk = k.shape
+    if tuple(v.shape) != tuple(k.shape) or Bk != B or dk != d:
+        raise ValueError("inconsistent q/k/v shapes")
+    if k.device != q.device or v.device != q.device:
+        raise ValueError("q, k, v must be on one device")
+    lens = _lens(kv_lens, B, q.device)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    o = out if out is not None else torch.empty_like(q)
+    _check_tensor("out", o, q.dtype)
+    if o.shape != q.shape:
+        raise ValueError("out must have q's shape")
+    stream = torch.cuda.current_stream(q.device).cuda_stream
+    st = attn_prefill_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), B, H_q, H_kv, S_q, S_kv, d,
+                          int(bool(causal)), float(scale), _ptr(lens), _DTYPES[q.dtype],
+                          ctypes.c_void_p(stream))
+    if st != 0:
+        raise AttnError(st, "attn_prefill_fwd")
+    return o
+
+
+def workspace_for(device, nbytes):
+    """Per-device scratch buffer of at least nbytes (grown on demand)."""
+    key = torch.device(device).index
+    ws = _workspaces.get(key)
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.empty(max(nbytes, 1 << 20), dtype=torch.uint8, device=device)
+        _workspaces[key] = ws
+    return ws
+
+
+def decode(q, k_cache, v_cache, kv_lens=None, scale=None, out=None, workspace=None):
+    """Single-query decode.  q [B,H_q,1,d]; k_cache, v_cache [B,H_kv,S_cap,d]
+    (bf16); kv_lens int32 [B] on the device (None: every row is valid).
+
+    Returns o [B,H_q,1,d] bf16.  Runs the split and combine kernels on torch's
+    current stream; the workspace (if not given) is cached per device.
+    """
+    for name, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache)):
+        _check_tensor(name, t, torch.bfloat16)
+        if t.dim() != 4:
+            raise ValueError(f"{name} must be [B, H, S, d]")
+    B, H_q, S_q, d = q.shape
+    Bk, H_kv, S_kv, dk = k_cache.shape
+    if tuple(v_cache.shape) != tuple(k_cache.shape) or Bk != B or dk != d:
+        raise ValueError("inconsistent q/k/v shapes")
+    lens = _lens(kv_lens, B, q.device)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    o = out if out is not None else torch.empty_like(q)
+    need = attn_decode_workspace_bytes(B, H_q, H_kv, S_kv, d)
+    ws = workspace if workspace is not None else workspace_for(q.device, need)
+    stream = torch.cuda.current_stream(q.device).cuda_stream
+    st = attn_decode_fwd(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(o), B, H_q, H_kv, S_q, S_kv,
+                         d, 0, float(scale), _ptr(lens), ATTN_BF16, _ptr(ws),
+                         ws.numel() * ws.element_size(), ctypes.c_void_p(stream))
+    if st != 0:
+        raise AttnError(st, "attn_decode_fwd")
+    return o

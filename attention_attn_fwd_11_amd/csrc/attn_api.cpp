@@ -1,0 +1,161 @@
+// attn_api.cpp -- the C ABI (include/attn.h): argument validation, launch
+// configuration and error reporting.  All checks run on the host before any
+// HIP call, so an invalid call launches nothing and touches no memory.
+#include "../../include/attn.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+
+#include "kernels.hpp"
+
+namespace {
+
+thread_local char g_hip_error[256] = "";
+
+attn_status_t hip_fail(const char* what, hipError_t e) {
+  std::snprintf(g_hip_error, sizeof g_hip_error, "%s: %s (%d)", what, hipGetErrorString(e), (int)e);
+  return ATTN_ERR_HIP;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Shared size checks for both entry points.
+attn_status_t check_common(const void* q, const void* k, const void* v, const void* o, int32_t B,
+                           int32_t H_q, int32_t H_kv, int32_t S_q, int32_t S_kv, int32_t d,
+                           int32_t causal, float scale, int dtype) {
+  if (B < 0 || S_q < 0 || S_kv < 0 || H_q < 1 || H_kv < 1 || d < 1) return ATTN_ERR_SHAPE;
+  if (H_q % H_kv != 0) return ATTN_ERR_SHAPE;
+  if (causal != 0 && causal != 1) return ATTN_ERR_SHAPE;
+  if (d != 64 && d != 128) return ATTN_ERR_UNSUPPORTED;
+  if (dtype != ATTN_F32 && dtype != ATTN_BF16) return ATTN_ERR_UNSUPPORTED;
+  if (!std::isfinite(scale)) return ATTN_ERR_VALUE;
+  const bool has_q = (int64_t)B * S_q > 0;
+  const bool has_kv = (int64_t)B * S_kv > 0;
+  if (has_q && (!q || !o)) return ATTN_ERR_NULL;
+  if (has_kv && (!k || !v)) return ATTN_ERR_NULL;
+  if ((q && !aligned16(q)) || (o && !aligned16(o)) || (k && !aligned16(k)) || (v && !aligned16(v)))
+    return ATTN_ERR_ALIGN;
+  // Offsets are formed in 64-bit arithmetic; each head's rows must fit int32 indexing of rows.
+  if ((int64_t)S_kv * d > INT32_MAX || (int64_t)S_q * d > INT32_MAX) return ATTN_ERR_SHAPE;
+  if ((int64_t)B * H_q > INT32_MAX / 2) return ATTN_ERR_SHAPE;
+  return ATTN_OK;
+}
+
+// Keys per decode split.  Test-only override: ATTN_DECODE_CHUNK (a positive
+// multiple of 256) forces the chunk so split-count invariance can be tested.
+int decode_chunk(int32_t B, int32_t H_kv, int32_t S_kv) {
+  if (const char* env = std::getenv("ATTN_DECODE_CHUNK")) {
+    const long c = std::strtol(env, nullptr, 10);
+    if (c >= 256 && c % 256 == 0 && c <= (1 << 30)) return (int)c;
+  }
+  // Aim for about 4096 workgroups (16 per compute unit on a 256-CU part) so
+  // the ragged tail of the last wave of workgroups stays short, but never
+  // split below 512 keys: each split costs a partial (d+1 floats) per query.
+  const int64_t heads = (int64_t)B * H_kv;
+  int64_t splits = heads >= 4096 ? 1 : (4096 + heads - 1) / heads;
+  const int64_t max_splits = (S_kv + 511) / 512;
+  if (splits > max_splits) splits = max_splits;
+  if (splits < 1) splits = 1;
+  int64_t chunk = (S_kv + splits - 1) / splits;
+  chunk = (chunk + 255) / 256 * 256;
+  if (chunk < 256) chunk = 256;
+  return (int)chunk;
+}
+
+size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+}  // namespace
+
+extern "C" {
+
+const char* attn_status_str(attn_status_t s) {
+  switch (s) {
+    case ATTN_OK: return "ok";
+    case ATTN_ERR_NULL: return "a required pointer is NULL";
+    case ATTN_ERR_SHAPE: return "inconsistent or invalid sizes";
+    case ATTN_ERR_UNSUPPORTED: return "unsupported head dimension or dtype";
+    case ATTN_ERR_ALIGN: return "pointer not 16-byte aligned";
+    case ATTN_ERR_WORKSPACE: return "decode workspace missing or too small";
+    case ATTN_ERR_HIP: return "HIP runtime error";
+    case ATTN_ERR_VALUE: return "non-finite scale";
+  }
+  return "unknown status";
+}
+
+const char* attn_last_hip_error(void) { return g_hip_error; }
+
+size_t attn_decode_workspace_bytes(int32_t B, int32_t H_q, int32_t H_kv, int32_t S_kv, int32_t d) {
+  if (B <= 0 || S_kv <= 0 || H_q < 1 || H_kv < 1 || H_q % H_kv != 0 || (d != 64 && d != 128))
+    return 0;
+  const int chunk = decode_chunk(B, H_kv, S_kv);
+  const int64_t n_split = (S_kv + chunk - 1) / chunk;
+  const size_t rows = (size_t)B * H_q * n_split;
+  return round_up(rows * d * sizeof(float), 256) + round_up(rows * sizeof(float), 256);
+}
+
+attn_status_t attn_prefill_fwd(const void* q, const void* k, const void* v, void* o, int32_t B,
+                               int32_t H_q, int32_t H_kv, int32_t S_q, int32_t S_kv, int32_t d,
+                               int32_t causal, float scale, const int32_t* kv_lens,
+                               attn_dtype_t dtype, void* stream) {
+  g_hip_error[0] = '\0';
+  attn_status_t st = check_common(q, k, v, o, B, H_q, H_kv, S_q, S_kv, d, causal, scale, dtype);
+  if (st != ATTN_OK) return st;
+  if (causal && S_q > S_kv) return ATTN_ERR_SHAPE;
+  if ((int64_t)B * S_q == 0) return ATTN_OK;  // nothing to compute
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (S_kv == 0) {
+    // every row sees no key: O = 0
+    const size_t elt = dtype == ATTN_F32 ? 4 : 2;
+    hipError_t e = attn::launch_zero_fill(o, (size_t)B * H_q * S_q * d * elt, s);
+    return e == hipSuccess ? ATTN_OK : hip_fail("zero-fill launch", e);
+  }
+  attn::PrefillParams p{};
+  p.q = q; p.k = k; p.v = v; p.o = o; p.kv_lens = kv_lens;
+  p.B = B; p.Hq = H_q; p.Hkv = H_kv; p.Sq = S_q; p.Skv = S_kv; p.d = d; p.causal = causal;
+  p.scale_log2 = (float)((double)scale * 1.4426950408889634);
+  hipError_t e = dtype == ATTN_F32 ? attn::launch_prefill_f32(p, s) : attn::launch_prefill_bf16(p, s);
+  return e == hipSuccess ? ATTN_OK : hip_fail("prefill launch", e);
+}
+
+attn_status_t attn_decode_fwd(const void* q, const void* k_cache, const void* v_cache, void* o,
+                              int32_t B, int32_t H_q, int32_t H_kv, int32_t S_q, int32_t S_kv,
+                              int32_t d, int32_t causal, float scale, const int32_t* kv_lens,
+                              attn_dtype_t dtype, void* workspace, size_t workspace_bytes,
+                              void* stream) {
+  g_hip_error[0] = '\0';
+  attn_status_t st = check_common(q, k_cache, v_cache, o, B, H_q, H_kv, S_q, S_kv, d, causal,
+                                  scale, dtype);
+  if (st != ATTN_OK) return st;
+  if (S_q != 1) return ATTN_ERR_SHAPE;
+  if (dtype != ATTN_BF16) return ATTN_ERR_UNSUPPORTED;
+  const int G = H_q / H_kv;
+  if (G != 1 && G != 2 && G != 4 && G != 8 && G != 16) return ATTN_ERR_UNSUPPORTED;
+  if (B == 0) return ATTN_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (S_kv == 0) {
+    hipError_t e = attn::launch_zero_fill(o, (size_t)B * H_q * d * 2, s);
+    return e == hipSuccess ? ATTN_OK : hip_fail("zero-fill launch", e);
+  }
+  const size_t need = attn_decode_workspace_bytes(B, H_q, H_kv, S_kv, d);
+  if (!workspace || workspace_bytes < need) return ATTN_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return ATTN_ERR_ALIGN;
+
+  attn::DecodeParams p{};
+  p.q = q; p.k = k_cache; p.v = v_cache; p.o = o; p.kv_lens = kv_lens;
+  p.B = B; p.Hq = H_q; p.Hkv = H_kv; p.Skv = S_kv; p.d = d;
+  p.chunk = decode_chunk(B, H_kv, S_kv);
+  p.n_split = (S_kv + p.chunk - 1) / p.chunk;
+  const size_t rows = (size_t)B * H_q * p.n_split;
+  p.part_o = static_cast<float*>(workspace);
+  p.part_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                        round_up(rows * d * sizeof(float), 256));
+  p.scale_log2 = (float)((double)scale * 1.4426950408889634);
+  hipError_t e = attn::launch_decode_bf16(p, s);
+  return e == hipSuccess ? ATTN_OK : hip_fail("decode launch", e);
+}
+
+}  // extern "C"

@@ -1,0 +1,435 @@
+// decode_bf16.hip -- single-query attention over a bf16 KV cache.
+//
+// Decoding as described in "Optimizing Decoder Attention for LLMs on GPU"
+// (magmadev.ru): one new query per head attends to every cached token, and
+// the step is bound by reading the cache, so each K/V element is read from
+// device memory exactly once per step.  The cache's sequence dimension is cut
+// into chunks processed in parallel (Flash-Decoding, "GPU learning day 24:
+// Operator Fusion", FAQ Q4); every chunk leaves a normalised partial output
+// and its log-sum-exp, and a second kernel merges the partials with the
+// rescaling identity of that page's section 3.4 loop.
+//
+// Kernels
+//   decode_split_valu<D>     one query head per KV head (no reuse of K/V
+//                            across queries: a streaming dot product, so the
+//                            vector ALU is the right unit).
+//   decode_split_mfma<D, G>  G >= 2 query heads share each KV head: the G
+//                            queries form a small matrix and QK^T and PV run on
+//                            v_mfma_f32_16x16x32_bf16 with the group padded to
+//                            16 rows.
+//   decode_combine<D>        merges the partials of one (batch, query head).
+//
+// Partial results are fp32; the log-sum-exp is kept in base-2 units
+// (scores are scaled by scale * log2(e)).  Chunks that start at or beyond a
+// sequence's length do no work and write nothing; the combine kernel derives
+// the number of valid chunks from the same length.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace attn {
+
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / 64;
+
+// Cross-wave merge of (m, l, o[D]) held by each wave's lanes, then the
+// partial is written by wave 0.  o_lane(d) gives this lane's share of o[d]
+// for the dims it owns (already summed within the wave).
+template <int D>
+struct WaveMerge {
+  float m[kWaves];
+  float l[kWaves];
+  float o[kWaves][D];
+};
+
+// ---------------------------------------------------------------------------
+// G = 1: vector-ALU split kernel.
+//
+// Lane layout: a key row is D/8 16-byte pieces; LPK = D/8 lanes cover one key
+// and a wave load instruction covers KPI = 64/LPK consecutive keys (1 KiB,
+// fully coalesced).  Per iteration a wave handles 8 instructions' worth of
+// keys (KB = 8*KPI).  The 8 partial dot products per lane are reduced across
+// the LPK lanes of a key with a halving exchange, which leaves every key's
+// full score in one lane (pair).
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(kThreads) void decode_split_valu(DecodeParams p) {
+  constexpr int LPK = D / 8;          // lanes per key row
+  constexpr int KPI = 64 / LPK;       // keys per load instruction
+  constexpr int KB = 8 * KPI;         // keys per wave iteration
+  constexpr int DUP = LPK / 8;        // lanes holding each reduced score (1 or 2)
+
+  __shared__ WaveMerge<D> merge;
+
+  const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  int n = p.Skv;
+  if (p.kv_lens) n = min(max(p.kv_lens[b], 0), p.Skv);
+  const int c0 = split * p.chunk;
+  if (c0 >= n) return;
+  const int c1 = min(c0 + p.chunk, n);
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int kg = lane / LPK;          // key within an instruction's group
+  const int dc = lane % LPK;          // 16-byte feature chunk
+  const uint16_t* kp = static_cast<const uint16_t*>(p.k) + ((int64_t)b * p.Hkv + h) * p.Skv * D;
+  const uint16_t* vp = static_cast<const uint16_t*>(p.v) + ((int64_t)b * p.Hkv + h) * p.Skv * D;
+  const u32x4 qv = ld16(static_cast<const uint16_t*>(p.q) + ((int64_t)b * p.Hq + h) * D + 8 * dc);
+
+  // Which of the 8 keys of this lane's group its reduced score belongs to.
+  const int my_u = (LPK == 16) ? ((lane >> 1) & 7) : (lane & 7);
+
+  float m = kNegInf, lsum = 0.f;
+  float o[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) o[e] = 0.f;
+
+  for (int base = c0 + wave * KB; base < c1; base += kWaves * KB) {
+    u32x4 kr[8], vr[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int key = min(base + u * KPI + kg, c1 - 1);
+      kr[u] = ld16(kp + (int64_t)key * D + 8 * dc);
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int key = min(base + u * KPI + kg, c1 - 1);
+      vr[u] = ld16(vp + (int64_t)key * D + 8 * dc);
+    }
+    // partial dots over this lane's 8 features
+    float part[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      float a = 0.f;
+#pragma unroll
+      for (int w = 0; w < 4; ++w)
+        a = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(qv[w]), as_bf16x2(kr[u][w]), a, false);
+      part[u] = a;
+    }
+    // halving exchange: 8 values over LPK lanes -> one full score per lane
+    // (pair).  Masks LPK/2, LPK/4, LPK/8 each halve the values a lane keeps;
+    // with LPK = 16 a last exchange over mask 1 completes the sum.
+    {
+      constexpr int MA = LPK / 2, MB = LPK / 4, MC = LPK / 8;
+      const bool ba = lane & MA;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const float send = ba ? part[t] : part[t + 4];
+        const float keep = ba ? part[t + 4] : part[t];
+        part[t] = keep + shfl_xor(send, MA);
+      }
+      const bool bb = lane & MB;
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const float send = bb ? part[t] : part[t + 2];
+        const float keep = bb ? part[t + 2] : part[t];
+        part[t] = keep + shfl_xor(send, MB);
+      }
+      const bool bc = lane & MC;
+      const float send = bc ? part[0] : part[1];
+      const float keep = bc ? part[1] : part[0];
+      part[0] = keep + shfl_xor(send, MC);
+      if (LPK == 16) part[0] += shfl_xor(part[0], 1);
+    }
+    float s = part[0];
+    const int my_key = base + my_u * KPI + kg;
+    s = (my_key < c1) ? s * p.scale_log2 : kNegInf;
+
+    // wave max
+    float t = s;
+#pragma unroll
+    for (int msk = 1; msk < 64; msk <<= 1) t = fmaxf(t, shfl_xor(t, msk));
+    const float m_new = fmaxf(m, t);
+    const float alpha = exp2_fast(m - m_new);   // m_new is finite: the block has a valid key
+    const float pr = exp2_fast(s - m_new);
+    m = m_new;
+    lsum = lsum * alpha + pr;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] *= alpha;
+    // o += sum_u p_u v_u over this lane's 8 keys
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int src = kg * LPK + ((LPK == 16) ? 2 * u : u);
+      const float pu = shfl(pr, src);
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        o[2 * w] = fmaf(pu, bf16_lo(vr[u][w]), o[2 * w]);
+        o[2 * w + 1] = fmaf(pu, bf16_hi(vr[u][w]), o[2 * w + 1]);
+      }
+    }
+  }
+
+  // Reduce within the wave: o over the KPI key groups, l over all lanes.
+#pragma unroll
+  for (int msk = LPK; msk < 64; msk <<= 1)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] += shfl_xor(o[e], msk);
+#pragma unroll
+  for (int msk = 1; msk < 64; msk <<= 1) lsum += shfl_xor(lsum, msk);
+  lsum *= 1.0f / DUP;
+
+  if (lane == 0) {
+    merge.m[wave] = m;
+    merge.l[wave] = lsum;
+  }
+  if (lane < LPK) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) merge.o[wave][8 * dc + e] = o[e];
+  }
+  __syncthreads();
+  if (wave == 0) {
+    float M = kNegInf;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, merge.m[w]);
+    float L = 0.f, wgt[kWaves];
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      wgt[w] = merge.m[w] == kNegInf ? 0.f : exp2_fast(merge.m[w] - M);
+      L += wgt[w] * merge.l[w];
+    }
+    const float invL = 1.f / L;
+    const int64_t prow = ((int64_t)b * p.Hq + h) * p.n_split + split;
+    for (int d = lane; d < D; d += 64) {
+      float acc = 0.f;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) acc += wgt[w] * merge.o[w][d];
+      p.part_o[prow * D + d] = acc * invL;
+    }
+    if (lane == 0) p.part_lse[prow] = M + log2_fast(L);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// G >= 2: matrix-core split kernel.
+//
+// Per 32-key step a wave computes S^T (32 keys x 16 query rows, rows >= G are
+// zero padding) with v_mfma_f32_16x16x32_bf16: K rows come straight from
+// device memory as the A operand (lane = key row, 8 features), Q^T is a
+// register-resident B operand.  Each lane then holds 8 keys of one query
+// column, which is already the B-operand layout of O^T += V^T P^T under a
+// fixed permutation of the 32 keys.  The wave stages its V rows in its own
+// LDS region (coalesced 16-byte stores) and reads V^T with the LDS transpose
+// read, so no workgroup barrier is needed inside the loop.
+// ---------------------------------------------------------------------------
+template <int D, int G>
+__global__ __launch_bounds__(kThreads) void decode_split_mfma(DecodeParams p) {
+  constexpr int KS = D / 32;          // k-steps of the score MFMA (32 features each)
+  constexpr int DT = D / 16;          // 16-feature output tiles
+  constexpr int SLOTS = D / 8;        // 16-byte slots per V row
+  constexpr int VBYTES = 32 * D * 2;  // one wave's V block
+  constexpr int VP = 32 * SLOTS / 64; // V pieces per lane per step
+
+  // V staging during the loop; reused afterwards for the cross-wave merge.
+  static_assert(kWaves * G * D * 4 <= kWaves * VBYTES, "merge buffer must fit the V buffers");
+  __shared__ __attribute__((aligned(16))) unsigned char vbuf[kWaves][VBYTES];
+  __shared__ float mrg_m[kWaves][16];
+  __shared__ float mrg_l[kWaves][16];
+  float (*mrg_o)[G][D] = reinterpret_cast<float (*)[G][D]>(&vbuf[0][0]);
+
+  const int split = blockIdx.x, hk = blockIdx.y, b = blockIdx.z;
+  int n = p.Skv;
+  if (p.kv_lens) n = min(max(p.kv_lens[b], 0), p.Skv);
+  const int c0 = split * p.chunk;
+  if (c0 >= n) return;
+  const int c1 = min(c0 + p.chunk, n);
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int qcol = lane & 15;          // query column (valid if < G)
+  const int grp = lane >> 4;           // 16-lane group
+  const uint16_t* kp = static_cast<const uint16_t*>(p.k) + ((int64_t)b * p.Hkv + hk) * p.Skv * D;
+  const uint16_t* vp = static_cast<const uint16_t*>(p.v) + ((int64_t)b * p.Hkv + hk) * p.Skv * D;
+
+  // Q^T as B operand: lane (qcol, grp) holds Q[h0 + qcol][32*ks + 8*grp .. +7].
+  bf16x8 qreg[KS];
+  {
+    const uint16_t* qp = static_cast<const uint16_t*>(p.q) + ((int64_t)b * p.Hq + (int64_t)hk * G) * D;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      u32x4 w = {0u, 0u, 0u, 0u};
+      if (qcol < G) w = ld16(qp + (int64_t)qcol * D + 32 * ks + 8 * grp);
+      qreg[ks] = as_bf16x8(w);
+    }
+  }
+
+  f32x4 oacc[DT];
+#pragma unroll
+  for (int t = 0; t < DT; ++t) oacc[t] = f32x4{};
+  float m = kNegInf, lsum = 0.f;
+  unsigned char* vb = vbuf[wave];
+
+  for (int base = c0 + wave * 32; base < c1; base += kWaves * 32) {
+    // K as A operand: lane (row = lane%16, grp) -> K[base + 16*hlf + row][32*ks + 8*grp ..]
+    u32x4 kr[2][KS];
+#pragma unroll
+    for (int hlf = 0; hlf < 2; ++hlf) {
+      const int key = min(base + 16 * hlf + qcol, c1 - 1);
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) kr[hlf][ks] = ld16(kp + (int64_t)key * D + 32 * ks + 8 * grp);
+    }
+    // V rows of this step: coalesced pieces, row = piece / SLOTS.
+    u32x4 vr[VP];
+#pragma unroll
+    for (int u = 0; u < VP; ++u) {
+      const int piece = u * 64 + lane;
+      const int row = piece / SLOTS, slot = piece % SLOTS;
+      const int key = min(base + row, c1 - 1);
+      vr[u] = ld16(vp + (int64_t)key * D + slot * 8);
+    }
+    // S^T for keys [base, base+16) and [base+16, base+32)
+    f32x4 sacc[2];
+#pragma unroll
+    for (int hlf = 0; hlf < 2; ++hlf) {
+      sacc[hlf] = f32x4{};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        sacc[hlf] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kr[hlf][ks]), qreg[ks], sacc[hlf], 0, 0, 0);
+    }
+    // stage V (wave-private LDS region, swizzled)
+#pragma unroll
+    for (int u = 0; u < VP; ++u) {
+      const int piece = u * 64 + lane;
+      const int row = piece / SLOTS, slot = piece % SLOTS;
+      *reinterpret_cast<u32x4*>(vb + (row * SLOTS + (slot ^ (row % SLOTS))) * 16) = vr[u];
+    }
+    // lane holds keys base + 16*hlf + 4*grp + i for query qcol
+    float tmax = kNegInf;
+#pragma unroll
+    for (int hlf = 0; hlf < 2; ++hlf)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int key = base + 16 * hlf + 4 * grp + i;
+        const float s = key < c1 ? sacc[hlf][i] * p.scale_log2 : kNegInf;
+        sacc[hlf][i] = s;
+        tmax = fmaxf(tmax, s);
+      }
+    tmax = fmaxf(tmax, shfl_xor(tmax, 16));
+    tmax = fmaxf(tmax, shfl_xor(tmax, 32));
+    const float m_new = fmaxf(m, tmax);            // finite: the step has a valid key
+    const float alpha = exp2_fast(m - m_new);
+    m = m_new;
+    uint32_t w[4];
+    float psum = 0.f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int hlf = e / 2, i0 = 2 * (e % 2);
+      w[e] = pack_bf16x2(exp2_fast(sacc[hlf][i0] - m_new), exp2_fast(sacc[hlf][i0 + 1] - m_new));
+      psum += bf16_lo(w[e]) + bf16_hi(w[e]);
+    }
+    lsum = lsum * alpha + psum;
+    const bf16x8 pb = as_bf16x8(u32x4{w[0], w[1], w[2], w[3]});
+#pragma unroll
+    for (int t = 0; t < DT; ++t) oacc[t] *= alpha;
+
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    // O^T += V^T P^T: the B operand's 8 keys are (4*grp + 0..3, 16 + 4*grp + 0..3)
+    const int src = lane & 15;
+#pragma unroll
+    for (int t = 0; t < DT; ++t) {
+      const int cidx = 16 * t + 4 * (src & 3);
+      const int cslot = cidx >> 3, cbyte = (cidx & 7) * 2;
+      const int r0 = 4 * grp + (src >> 2);
+      const int r1 = r0 + 16;
+      const u32x2 lo = lds_read_tr16x4(vb + (r0 * SLOTS + (cslot ^ (r0 % SLOTS))) * 16 + cbyte);
+      const u32x2 hi = lds_read_tr16x4(vb + (r1 * SLOTS + (cslot ^ (r1 % SLOTS))) * 16 + cbyte);
+      oacc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]}), pb, oacc[t], 0, 0, 0);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  }
+
+  // l per query: sum over the 4 lane groups holding the same query column.
+  lsum += shfl_xor(lsum, 16);
+  lsum += shfl_xor(lsum, 32);
+  // O^T accumulator: lane (qcol, grp) holds features 16*t + 4*grp + i.
+  if (lane < 16) {
+    mrg_m[wave][qcol] = m;
+    mrg_l[wave][qcol] = lsum;
+  }
+  __syncthreads();   // every wave is done with its V buffer before it is reused
+  if (qcol < G) {
+#pragma unroll
+    for (int t = 0; t < DT; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) mrg_o[wave][qcol][16 * t + 4 * grp + i] = oacc[t][i];
+  }
+  __syncthreads();
+  // merge the waves: thread tid handles (query, feature) pairs
+  for (int idx = tid; idx < G * D; idx += kThreads) {
+    const int qi = idx / D, d = idx % D;
+    float M = kNegInf;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, mrg_m[w][qi]);
+    float L = 0.f, acc = 0.f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      const float wt = mrg_m[w][qi] == kNegInf ? 0.f : exp2_fast(mrg_m[w][qi] - M);
+      L += wt * mrg_l[w][qi];
+      acc += wt * mrg_o[w][qi][d];
+    }
+    const int64_t prow = ((int64_t)b * p.Hq + (int64_t)hk * G + qi) * p.n_split + split;
+    p.part_o[prow * D + d] = acc / L;
+    if (d == 0) p.part_lse[prow] = M + log2_fast(L);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Combine: O = sum_s 2^(lse_s - M) o_s / sum_s 2^(lse_s - M), M = max_s lse_s.
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(64) void decode_combine(DecodeParams p) {
+  const int h = blockIdx.x, b = blockIdx.y;
+  const int lane = threadIdx.x;
+  int n = p.Skv;
+  if (p.kv_lens) n = min(max(p.kv_lens[b], 0), p.Skv);
+  const int ns = (n + p.chunk - 1) / p.chunk;
+  uint16_t* orow = static_cast<uint16_t*>(p.o) + ((int64_t)b * p.Hq + h) * D;
+  const int64_t prow0 = ((int64_t)b * p.Hq + h) * p.n_split;
+  constexpr int PER = D / 64;
+  float acc[PER];
+#pragma unroll
+  for (int e = 0; e < PER; ++e) acc[e] = 0.f;
+  float M = kNegInf;
+  for (int s = 0; s < ns; ++s) M = fmaxf(M, p.part_lse[prow0 + s]);
+  float W = 0.f;
+  for (int s = 0; s < ns; ++s) {
+    const float wt = exp2_fast(p.part_lse[prow0 + s] - M);
+    W += wt;
+#pragma unroll
+    for (int e = 0; e < PER; ++e) acc[e] = fmaf(wt, p.part_o[(prow0 + s) * D + PER * lane + e], acc[e]);
+  }
+  const float inv = ns > 0 ? 1.f / W : 0.f;
+  if (PER == 2) {
+    reinterpret_cast<uint32_t*>(orow)[lane] = pack_bf16x2(acc[0] * inv, acc[PER - 1] * inv);
+  } else {
+    orow[lane] = f32_to_bf16_bits(acc[0] * inv);
+  }
+}
+
+template <int D>
+hipError_t launch_d(const DecodeParams& p, hipStream_t stream) {
+  const int G = p.Hq / p.Hkv;
+  dim3 grid(p.n_split, p.Hkv, p.B);
+  switch (G) {
+    case 1: hipLaunchKernelGGL((decode_split_valu<D>), grid, dim3(kThreads), 0, stream, p); break;
+    case 2: hipLaunchKernelGGL((decode_split_mfma<D, 2>), grid, dim3(kThreads), 0, stream, p); break;
+    case 4: hipLaunchKernelGGL((decode_split_mfma<D, 4>), grid, dim3(kThreads), 0, stream, p); break;
+    case 8: hipLaunchKernelGGL((decode_split_mfma<D, 8>), grid, dim3(kThreads), 0, stream, p); break;
+    case 16: hipLaunchKernelGGL((decode_split_mfma<D, 16>), grid, dim3(kThreads), 0, stream, p); break;
+    default: return hipErrorInvalidValue;
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((decode_combine<D>), dim3(p.Hq, p.B), dim3(64), 0, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_decode_bf16(const DecodeParams& p, hipStream_t stream) {
+  return p.d == 64 ? launch_d<64>(p, stream) : launch_d<128>(p, stream);
+}
+
+}  // namespace attn

@@ -1,0 +1,42 @@
+// kernels.hpp -- host-side launch interface between the C ABI layer and the
+// kernels.  Every launcher assumes its arguments were validated by the ABI
+// layer (sizes, alignment, supported d and dtype) and only enqueues work.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace attn {
+
+struct PrefillParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  const int32_t* kv_lens;  // device int32[B] or nullptr
+  int B, Hq, Hkv, Sq, Skv, d;
+  int causal;
+  float scale_log2;        // scale * log2(e)
+};
+
+struct DecodeParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  const int32_t* kv_lens;  // device int32[B] or nullptr
+  float* part_o;           // [B, Hq, n_split, d] fp32
+  float* part_lse;         // [B, Hq, n_split]   fp32, base-2 log-sum-exp
+  int B, Hq, Hkv, Skv, d;
+  int chunk;               // keys per split (multiple of 256)
+  int n_split;
+  float scale_log2;
+};
+
+hipError_t launch_prefill_f32(const PrefillParams& p, hipStream_t stream);
+hipError_t launch_prefill_bf16(const PrefillParams& p, hipStream_t stream);
+hipError_t launch_decode_bf16(const DecodeParams& p, hipStream_t stream);
+hipError_t launch_zero_fill(void* dst, size_t bytes, hipStream_t stream);
+
+}  // namespace attn

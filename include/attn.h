@@ -1,0 +1,138 @@
+/*
+ * attn.h -- C ABI of the fused attention forward pass for MI355X (gfx950).
+ *
+ * The operation is exact softmax attention, O = softmax(Q K^T * scale + mask) V,
+ * as defined in "GPU learning day 24: Operator Fusion" (daoyuly.cn), section
+ * 3.4 (the standard attention block: scores, scaling and mask, softmax, P V),
+ * and computed the way that section's FlashAttention loop does: K/V blocks
+ * streamed through on-chip memory with a running row max and row sum, so the
+ * score matrix is never written to device memory.  Decode follows "Optimizing
+ * Decoder Attention for LLMs on GPU" (magmadev.ru), structure of attention in
+ * decoding mode (one new query attends to all cached tokens), with the KV
+ * sequence split into parallel parts as in the first page's FAQ Q4
+ * (Flash-Decoding) and the parts merged by their log-sum-exp.
+ *
+ * Conventions shared by every entry point
+ *   - Layout: contiguous row-major, head dimension innermost.
+ *       Q, O : [B, H_q,  S_q,  d]
+ *       K, V : [B, H_kv, S_kv, d]
+ *     O has Q's dtype.  Accumulation is fp32 for every dtype.
+ *   - Grouped-query attention: query head h reads KV head h / (H_q / H_kv).
+ *   - Masking: the dot product is multiplied by `scale` first; masked keys
+ *     then get weight exactly 0.  With kv_lens, batch b sees only its first
+ *     n_b = clamp(kv_lens[b], 0, S_kv) keys.  `causal` aligns the mask to the
+ *     bottom right: query i sees key j iff j <= i + n_b - S_q.  A row that sees
+ *     no key is written as 0.
+ *   - Pointers: device pointers, 16-byte aligned.  Buffers are owned by the
+ *     caller; the library allocates nothing, keeps no pointer after a call
+ *     returns, and only enqueues work on `stream` (a hipStream_t; NULL means
+ *     the null stream).  The caller keeps buffers alive until the stream has
+ *     run the work.  A pointer may be NULL only when its tensor has no
+ *     elements.
+ *   - kv_lens: device int32[B] or NULL (NULL: every batch has S_kv keys).
+ *     Its values are read on the device and clamped to [0, S_kv]; the host
+ *     cannot check them without synchronising, so this is a precondition.
+ *   - Errors: every function returns a status and never aborts or throws.
+ *     All validation runs on the host before anything is launched; on any
+ *     error nothing is launched and O is untouched.  ATTN_ERR_HIP means a HIP
+ *     call failed; attn_last_hip_error() then names it.
+ *   - Thread safety: the library is stateless apart from a per-device cache
+ *     of the compute-unit count (filled once) and a thread-local error string.
+ *     Concurrent calls on different streams are safe.
+ */
+#ifndef ATTN_H
+#define ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    ATTN_OK = 0,
+    ATTN_ERR_NULL = 1,        /* a required pointer is NULL                      */
+    ATTN_ERR_SHAPE = 2,       /* inconsistent or negative sizes                  */
+    ATTN_ERR_UNSUPPORTED = 3, /* valid but not implemented: d, dtype             */
+    ATTN_ERR_ALIGN = 4,       /* a pointer is not 16-byte aligned                */
+    ATTN_ERR_WORKSPACE = 5,   /* decode workspace missing or too small           */
+    ATTN_ERR_HIP = 6,         /* a HIP runtime call or kernel launch failed      */
+    ATTN_ERR_VALUE = 7        /* non-finite scale                                */
+} attn_status_t;
+
+typedef enum {
+    ATTN_F32 = 0,   /* IEEE binary32 in and out                             */
+    ATTN_BF16 = 1   /* bfloat16 in and out (round to nearest even on output) */
+} attn_dtype_t;
+
+/*
+ * Prefill (and general) attention forward.
+ *
+ *   q [B,H_q,S_q,d], k/v [B,H_kv,S_kv,d], o [B,H_q,S_q,d]   (device, dtype)
+ *   B >= 0, S_q >= 0, S_kv >= 0, H_q >= 1, H_kv >= 1, H_q % H_kv == 0.
+ *   d: 64 or 128.
+ *   causal: 0 or 1; causal with S_q > S_kv is rejected (ATTN_ERR_SHAPE).
+ *   scale: finite; the usual value is 1/sqrt(d).
+ *   kv_lens: see above.
+ *   dtype: ATTN_F32 or ATTN_BF16.  bf16 runs QK^T and PV on bf16 matrix cores
+ *   with fp32 accumulation and rounds P to bf16 before PV; fp32 computes in
+ *   fp32 throughout.
+ *
+ * Defined by the standard-attention block of "GPU learning day 24: Operator
+ * Fusion", section 3.4, and computed by that section's tiled online-softmax
+ * loop.
+ */
+attn_status_t attn_prefill_fwd(const void* q, const void* k, const void* v, void* o,
+                               int32_t B, int32_t H_q, int32_t H_kv, int32_t S_q, int32_t S_kv,
+                               int32_t d, int32_t causal, float scale, const int32_t* kv_lens,
+                               attn_dtype_t dtype, void* stream);
+
+/*
+ * Single-query decode over a KV cache.
+ *
+ *   q [B,H_q,1,d], o [B,H_q,1,d]; k_cache/v_cache [B,H_kv,S_kv,d] where S_kv is
+ *   the cache capacity (the row stride between heads); batch b attends to its
+ *   first clamp(kv_lens[b], 0, S_kv) rows.
+ *   S_q must be 1 (else ATTN_ERR_SHAPE).  causal is accepted and has no
+ *   effect with one query row (the bottom-right mask then allows every key).
+ *   dtype: ATTN_BF16 only (else ATTN_ERR_UNSUPPORTED).  d: 64 or 128.
+ *   workspace: device memory of at least
+ *   attn_decode_workspace_bytes(B, H_q, H_kv, S_kv, d) bytes, 16-byte
+ *   aligned, for the per-split partial results (fp32).  Its contents need no
+ *   initialisation and are scratch after the call.  Two calls that share a
+ *   workspace must be ordered on one stream.
+ *
+ * Two kernels on `stream`: a split pass in which each workgroup streams one
+ * chunk of the cache once and writes a normalised partial output with its
+ * log-sum-exp, then a combine pass that merges the partials of each head.
+ * This is the Flash-Decoding split of "GPU learning day 24: Operator Fusion",
+ * FAQ Q4, merged with the rescaling identity of that page's section 3.4 loop.
+ */
+attn_status_t attn_decode_fwd(const void* q, const void* k_cache, const void* v_cache, void* o,
+                              int32_t B, int32_t H_q, int32_t H_kv, int32_t S_q, int32_t S_kv,
+                              int32_t d, int32_t causal, float scale, const int32_t* kv_lens,
+                              attn_dtype_t dtype, void* workspace, size_t workspace_bytes,
+                              void* stream);
+
+/*
+ * Workspace bytes attn_decode_fwd needs for these sizes (0 if the sizes are
+ * invalid or the problem is empty).  Pure host function; no HIP call.
+ */
+size_t attn_decode_workspace_bytes(int32_t B, int32_t H_q, int32_t H_kv, int32_t S_kv, int32_t d);
+
+/* Static, NUL-terminated description of a status code. */
+const char* attn_status_str(attn_status_t s);
+
+/*
+ * Text of the last HIP error seen by an attn_* call on this thread (the
+ * failing call and hipGetErrorString), or "" if none.  Valid until the next
+ * attn_* call on the same thread.
+ */
+const char* attn_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTN_H */

@@ -1,0 +1,107 @@
+"""C ABI checks that need no GPU: the library loads, exports every function
+include/attn.h declares, and rejects invalid arguments on the host before
+any HIP call (so no kernel is ever launched here)."""
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+import attention_attn_fwd_11_amd as attn
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "attn.h")
+
+NULL = None
+P = ctypes.c_void_p(0x10000)       # a 16-byte aligned dummy address, never dereferenced
+MIS = ctypes.c_void_p(0x10008)     # misaligned
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(attn_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(attn.library_path):
+        pytest.skip("libattn.so not built (run __graft_entry__.build())")
+    return attn._load()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert {"attn_prefill_fwd", "attn_decode_fwd", "attn_decode_workspace_bytes",
+            "attn_status_str", "attn_last_hip_error"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), f"libattn.so does not export {n}"
+
+
+def test_status_strings(lib):
+    for code in range(0, 8):
+        s = attn.attn_status_str(code)
+        assert s and s != "unknown status"
+    assert attn.attn_status_str(99) == "unknown status"
+
+
+def prefill(q=P, k=P, v=P, o=P, B=1, Hq=2, Hkv=2, Sq=8, Skv=8, d=64, causal=1, scale=0.125,
+            lens=NULL, dtype=attn.ATTN_BF16):
+    return attn.attn_prefill_fwd(q, k, v, o, B, Hq, Hkv, Sq, Skv, d, causal, scale, lens, dtype,
+                                 NULL)
+
+
+def decode(q=P, k=P, v=P, o=P, B=1, Hq=2, Hkv=2, Sq=1, Skv=8, d=64, causal=0, scale=0.125,
+           lens=NULL, dtype=attn.ATTN_BF16, ws=P, wsb=1 << 30):
+    return attn.attn_decode_fwd(q, k, v, o, B, Hq, Hkv, Sq, Skv, d, causal, scale, lens, dtype, ws,
+                                wsb, NULL)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=NULL), 1), (dict(k=NULL), 1), (dict(v=NULL), 1), (dict(o=NULL), 1),
+    (dict(B=-1), 2), (dict(Sq=-1), 2), (dict(Skv=-2), 2), (dict(Hq=0), 2), (dict(Hkv=0), 2),
+    (dict(Hq=6, Hkv=4), 2), (dict(causal=2), 2), (dict(Sq=9, Skv=8, causal=1), 2),
+    (dict(d=96), 3), (dict(d=256), 3), (dict(dtype=5), 3),
+    (dict(q=MIS), 4), (dict(o=MIS), 4), (dict(k=MIS), 4), (dict(v=MIS), 4),
+    (dict(scale=math.inf), 7), (dict(scale=math.nan), 7),
+])
+def test_prefill_rejects(lib, kw, code):
+    assert prefill(**kw) == code
+
+
+def test_prefill_empty_is_noop(lib):
+    # nothing to compute: succeeds without touching the device
+    assert prefill(q=NULL, o=NULL, B=0) == 0
+    assert prefill(q=NULL, o=NULL, Sq=0) == 0
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=NULL), 1), (dict(o=NULL), 1), (dict(k=NULL), 1),
+    (dict(Sq=2), 2), (dict(Sq=0), 2), (dict(Hq=6, Hkv=4), 2), (dict(B=-3), 2),
+    (dict(dtype=attn.ATTN_F32), 3), (dict(d=32), 3), (dict(Hq=6, Hkv=2), 3), (dict(Hq=64, Hkv=2), 3),
+    (dict(ws=NULL), 5), (dict(wsb=16), 5), (dict(ws=MIS), 4), (dict(k=MIS), 4),
+    (dict(scale=-math.inf), 7),
+])
+def test_decode_rejects(lib, kw, code):
+    assert decode(**kw) == code
+
+
+def test_workspace_bytes(lib):
+    ws = attn.attn_decode_workspace_bytes
+    assert ws(0, 32, 32, 4096, 128) == 0
+    assert ws(1, 6, 4, 64, 128) == 0
+    assert ws(1, 32, 32, 4096, 96) == 0
+    a = ws(64, 32, 32, 4096, 128)
+    assert a > 0 and a % 256 == 0
+    # grows with heads and capacity; covers at least one partial per query head
+    assert ws(64, 32, 32, 8192, 128) >= a
+    assert ws(2, 4, 1, 100, 64) >= 2 * 4 * (64 + 1) * 4
+
+
+def test_workspace_follows_chunk_override(lib, monkeypatch):
+    base = attn.attn_decode_workspace_bytes(1, 4, 1, 4096, 128)
+    monkeypatch.setenv("ATTN_DECODE_CHUNK", "256")
+    forced = attn.attn_decode_workspace_bytes(1, 4, 1, 4096, 128)
+    # 16 splits of 256 keys: 4 heads x 16 x (128 + 1) floats
+    assert forced >= 4 * 16 * 129 * 4 and forced >= base
