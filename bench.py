@@ -1,0 +1,220 @@
+"""Benchmark of the fused attention forward on one MI355X.
+
+One step is one pass of the whole hot path on its headline shapes:
+  - causal prefill, bf16, B=4, H=32, S=4096, d=128  (the headline workload)
+  - single-query decode over a bf16 KV cache, B=64, H=32, L=4096, d=128
+    (split-KV pass + log-sum-exp combine).
+Inputs are seeded synthetic tensors already resident in device memory when
+the timed region starts.  W untimed warm-up steps are followed by K timed
+steps between device synchronisations; inside them every kernel call is
+bracketed by HIP events on the stream it is launched on.
+
+Printed: one JSON line.  `value` is prefill TFLOP/s (algorithmic FLOPs: 4*d
+per visible query/key pair) over the prefill kernel's average event time;
+decode KV-read GB/s (algorithmic K+V bytes, every visible row once) is given
+beside it, with a roofline object for each against MI355X's published peaks
+(dense bf16 MFMA 2516.6 TFLOP/s, HBM 8 TB/s).  The remaining workloads
+(GQA ragged decode, long GQA prefill) are timed the same way and reported
+under "other_workloads".  The CPU oracle is timed on a bounded sample of the
+prefill workload as "cpu_baseline".
+"""
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6      # 256 CUs x 4096 FLOP/clk x 2.4 GHz, dense
+PEAK_HBM_GBPS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true",
+                    help="skip timing the CPU oracle (e.g. under a profiler)")
+    ap.add_argument("--no-others", action="store_true",
+                    help="time only the headline step (prefill + MHA decode)")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="target CPU time for the oracle sample")
+    return ap.parse_args()
+
+
+class Timer:
+    """Accumulates HIP-event time of repeated calls on the current stream."""
+
+    def __init__(self, torch):
+        self.torch = torch
+        self.pairs = []
+
+    def __call__(self, fn):
+        t = self.torch
+        a = t.cuda.Event(enable_timing=True)
+        b = t.cuda.Event(enable_timing=True)
+        a.record()
+        fn()
+        b.record()
+        self.pairs.append((a, b))
+
+    def mean_ms(self):
+        ts = [a.elapsed_time(b) for a, b in self.pairs]
+        return sum(ts) / len(ts), ts
+
+
+def cpu_baseline(w, x, seconds):
+    """Time the fp64 oracle on a growing sample of prefill rows (random
+    (b, h, i) triples) until about `seconds` of wall time; report its rate
+    in the same algorithmic unit as the GPU figure."""
+    import numpy as np
+    import oracle
+
+    q, k, v = x["q"].cpu(), x["k"].cpu(), x["v"].cpu()
+    g = np.random.default_rng(0)
+    rows_done, flops, elapsed = 0, 0, 0.0
+    batch = 64
+    while elapsed < seconds:
+        rows = np.stack([g.integers(0, w.B, batch), g.integers(0, w.Hq, batch),
+                         g.integers(0, w.Sq, batch)], axis=1)
+        t0 = time.perf_counter()
+        oracle.attention_rows(q, k, v, w.causal, w.scale, rows)
+        elapsed += time.perf_counter() - t0
+        # visible keys of row i (causal, S_q = S_kv): i + 1
+        flops += int(sum(4 * w.d * (int(i) + 1 if w.causal else w.Skv) for i in rows[:, 2]))
+        rows_done += batch
+        batch = min(batch * 2, 4096)
+    return {
+        "value": flops / elapsed / 1e12,
+        "unit": "TFLOP/s",
+        "cores": oracle.num_threads(),
+        "kind": "oracle",
+        "sample": f"{rows_done} random (b, h, i) query rows of the prefill workload "
+                  f"({flops / 1e9:.1f} GFLOP fp64, {elapsed:.1f} s)",
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); this build has no "
+              "multi-GPU path: every workload here runs on a single MI355X.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import attention_attn_fwd_11_amd as attn
+    from attention_attn_fwd_11_amd import workloads as wl
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+
+    wp = wl.BY_NAME["prefill_bf16_b4h32s4096"]
+    wd = wl.BY_NAME["decode_bf16_b64h32l4096"]
+    others = [] if args.no_others else [wl.BY_NAME["decode_gqa_bf16_b128h32kv8"],
+                                        wl.BY_NAME["prefill_gqa_bf16_h64kv8s16384"]]
+    inputs = {w.name: wl.generate(w, dev) for w in [wp, wd, *others]}
+    torch.cuda.synchronize()
+
+    def call(w):
+        x = inputs[w.name]
+        if w.kind == "prefill":
+            return lambda: attn.prefill(x["q"], x["k"], x["v"], causal=w.causal, scale=w.scale,
+                                        out=x.setdefault("o", torch.empty_like(x["q"])))
+        return lambda: attn.decode(x["q"], x["k"], x["v"], kv_lens=x["kv_lens"], scale=w.scale,
+                                   out=x.setdefault("o", torch.empty_like(x["q"])))
+
+    fp, fd = call(wp), call(wd)
+    for _ in range(args.warmup):
+        fp()
+        fd()
+    torch.cuda.synchronize()
+
+    tp, td = Timer(torch), Timer(torch)
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        tp(fp)
+        td(fd)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_p, _ = tp.mean_ms()
+    ms_d, _ = td.mean_ms()
+
+    flops_p = wl.prefill_flops(wp)
+    bytes_d = wl.decode_kv_bytes(wd, inputs[wd.name]["kv_lens"].cpu())
+    tflops = flops_p / (ms_p * 1e-3) / 1e12
+    gbps = bytes_d / (ms_d * 1e-3) / 1e9
+
+    other = {}
+    for w in others:
+        f = call(w)
+        for _ in range(args.warmup):
+            f()
+        torch.cuda.synchronize()
+        tm = Timer(torch)
+        for _ in range(args.steps):
+            tm(f)
+        torch.cuda.synchronize()
+        ms, _ = tm.mean_ms()
+        if w.kind == "prefill":
+            fl = wl.prefill_flops(w)
+            rate = fl / (ms * 1e-3) / 1e12
+            other[w.name] = {"shape": w.describe(), "ms": round(ms, 4), "TFLOP/s": round(rate, 1),
+                             "frac_of_mfma_peak": round(rate / PEAK_BF16_TFLOPS, 4),
+                             "algorithmic_flop": fl}
+        else:
+            by = wl.decode_kv_bytes(w, inputs[w.name]["kv_lens"].cpu())
+            rate = by / (ms * 1e-3) / 1e9
+            other[w.name] = {"shape": w.describe(), "ms": round(ms, 4), "GB/s": round(rate, 1),
+                             "frac_of_hbm_peak": round(rate / PEAK_HBM_GBPS, 4),
+                             "algorithmic_bytes": by}
+
+    roof_p = {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS,
+              "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4), "traffic": None,
+              "kernel": "prefill_bf16_kernel<128, causal>", "avg_launch_ms": round(ms_p, 4),
+              "algorithmic_per_launch": flops_p}
+    roof_d = {"bound": "hbm", "achieved": round(gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+              "frac": round(gbps / PEAK_HBM_GBPS, 4), "traffic": None,
+              "kernel": "decode_split_valu<128> + decode_combine<128>",
+              "avg_launch_ms": round(ms_d, 4), "algorithmic_per_launch": bytes_d}
+    dominant, second = (roof_p, roof_d) if ms_p >= ms_d else (roof_d, roof_p)
+
+    out = {
+        "metric": "prefill attention TFLOPS + decode KV GB/s, % of MI355X peak (1 GPU)",
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3 / args.steps, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1), generated on the device)",
+        "config": {
+            "workload": "causal prefill bf16 B4 H32 S4096 d128 + decode bf16 B64 H32 L4096 d128",
+            "prefill": wp.describe(), "decode": wd.describe(),
+            "prefill_ms": round(ms_p, 4), "decode_ms": round(ms_d, 4),
+        },
+        "prefill_tflops": round(tflops, 2),
+        "prefill_frac_of_mfma_peak": round(tflops / PEAK_BF16_TFLOPS, 4),
+        "decode_kv_gbps": round(gbps, 1),
+        "decode_frac_of_hbm_peak": round(gbps / PEAK_HBM_GBPS, 4),
+        "roofline": dominant,
+        "roofline_other": second,
+        "other_workloads": other,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(wp, inputs[wp.name], args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()
