@@ -19,6 +19,7 @@ typedef __attribute__((address_space(3))) uint16_t lds_u16;
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kNegInf = -__builtin_huge_valf();
+constexpr float kPosInf = __builtin_huge_valf();
 
 // Hardware base-2 exponential (v_exp_f32).
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
@@ -32,9 +33,12 @@ __device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
   return __builtin_bit_cast(uint16_t, h);
 }
 
-// Two fp32 -> one dword of two bf16 (lo in bits 0..15), round to nearest even.
+// Two fp32 -> one dword of two bf16 (lo in bits 0..15), round to nearest
+// even, in one v_cvt_pk_bf16_f32.
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return (uint32_t)f32_to_bf16_bits(lo) | ((uint32_t)f32_to_bf16_bits(hi) << 16);
+  typedef float f32x2_t __attribute__((ext_vector_type(2)));
+  const f32x2_t v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
 }
 
 // bf16 halves of a dword -> fp32 (exact).
@@ -50,6 +54,9 @@ __device__ __forceinline__ void st16(void* p, u32x4 v) { *reinterpret_cast<u32x4
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 __device__ __forceinline__ bf16x2 as_bf16x2(uint32_t v) { return __builtin_bit_cast(bf16x2, v); }
 
+// (1.0, 1.0) in bf16: dot2 with it sums the two halves of a packed pair.
+#define kOnesBf16x2 (as_bf16x2(0x3f803f80u))
+
 // LDS transpose read (ds_read_b64_tr_b16).  Within each 16-lane group the
 // four rows x sixteen columns of 16-bit elements addressed by the group are
 // transposed: source lane s supplies the address of row s/4, columns
@@ -59,6 +66,46 @@ __device__ __forceinline__ u32x2 lds_read_tr16x4(const void* lds_generic) {
   const lds_i16x4* p = (const lds_i16x4*)(const __attribute__((address_space(3))) void*)lds_generic;
   i16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(const_cast<lds_i16x4*>(p));
   return __builtin_bit_cast(u32x2, r);
+}
+
+// LDS byte swizzle at 16-byte granularity for row-major tiles of 8..16
+// 16-byte slots per row.  Row r's slot s is stored at slot s ^ sw(r) with
+// sw(r) = 2*(r&3) | ((r>>2)&1) | (r&8).  Two access patterns are then free of
+// bank conflicts: 8 consecutive rows reading the same slot (a permutation of
+// slot%8 over the rows) and 4 consecutive rows (aligned to 4) reading the same
+// even-aligned slot pair (the transpose reads: the pair index moves by r&3).
+__device__ __forceinline__ int lds_swizzle(int row) {
+  return ((row & 3) << 1) | ((row >> 2) & 1) | (row & 8);
+}
+
+// Direct global -> LDS copy of 16 bytes per lane (global_load_lds_dwordx4):
+// lane i's 16 bytes land at lds_base + 16*i; lds_base must be wave-uniform.
+typedef __attribute__((address_space(3))) void lds_void;
+__device__ __forceinline__ void global_to_lds16(const void* g, void* lds_base) {
+  __builtin_amdgcn_global_load_lds(g, (lds_void*)lds_base, 16, 0, 0);
+}
+
+// Waits for this wave's outstanding vector-memory loads (including direct
+// global -> LDS copies).
+__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Value of lane l^32 (the other half of the wave), via v_permlane32_swap:
+// a VALU op, so no trip through the LDS crossbar.  swap(x, x) yields
+// {x of lanes 0-31 in both halves, x of lanes 32-63 in both halves}.
+__device__ __forceinline__ float max_across_halves(float x) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, x);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return fmaxf(__builtin_bit_cast(float, (uint32_t)r[0]), __builtin_bit_cast(float, (uint32_t)r[1]));
+}
+__device__ __forceinline__ float min_across_halves(float x) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, x);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return fminf(__builtin_bit_cast(float, (uint32_t)r[0]), __builtin_bit_cast(float, (uint32_t)r[1]));
+}
+__device__ __forceinline__ float sum_across_halves(float x) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, x);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return __builtin_bit_cast(float, (uint32_t)r[0]) + __builtin_bit_cast(float, (uint32_t)r[1]);
 }
 
 // Lane-exchange helpers (wave64).

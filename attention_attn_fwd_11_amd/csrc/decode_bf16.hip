@@ -208,8 +208,9 @@ __global__ __launch_bounds__(kThreads) void decode_split_valu(DecodeParams p) {
 // register-resident B operand.  Each lane then holds 8 keys of one query
 // column, which is already the B-operand layout of O^T += V^T P^T under a
 // fixed permutation of the 32 keys.  The wave stages its V rows in its own
-// LDS region (coalesced 16-byte stores) and reads V^T with the LDS transpose
-// read, so no workgroup barrier is needed inside the loop.
+// LDS region (coalesced 16-byte stores, rows swizzled by lds_swizzle) and
+// reads V^T with the LDS transpose read, so no workgroup barrier is needed
+// inside the loop.
 // ---------------------------------------------------------------------------
 template <int D, int G>
 __global__ __launch_bounds__(kThreads) void decode_split_mfma(DecodeParams p) {
@@ -289,7 +290,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_mfma(DecodeParams p) {
     for (int u = 0; u < VP; ++u) {
       const int piece = u * 64 + lane;
       const int row = piece / SLOTS, slot = piece % SLOTS;
-      *reinterpret_cast<u32x4*>(vb + (row * SLOTS + (slot ^ (row % SLOTS))) * 16) = vr[u];
+      *reinterpret_cast<u32x4*>(vb + (row * SLOTS + (slot ^ (lds_swizzle(row) & (SLOTS - 1)))) * 16) = vr[u];
     }
     // lane holds keys base + 16*hlf + 4*grp + i for query qcol
     float tmax = kNegInf;
@@ -331,8 +332,8 @@ __global__ __launch_bounds__(kThreads) void decode_split_mfma(DecodeParams p) {
       const int cslot = cidx >> 3, cbyte = (cidx & 7) * 2;
       const int r0 = 4 * grp + (src >> 2);
       const int r1 = r0 + 16;
-      const u32x2 lo = lds_read_tr16x4(vb + (r0 * SLOTS + (cslot ^ (r0 % SLOTS))) * 16 + cbyte);
-      const u32x2 hi = lds_read_tr16x4(vb + (r1 * SLOTS + (cslot ^ (r1 % SLOTS))) * 16 + cbyte);
+      const u32x2 lo = lds_read_tr16x4(vb + (r0 * SLOTS + (cslot ^ (lds_swizzle(r0) & (SLOTS - 1)))) * 16 + cbyte);
+      const u32x2 hi = lds_read_tr16x4(vb + (r1 * SLOTS + (cslot ^ (lds_swizzle(r1) & (SLOTS - 1)))) * 16 + cbyte);
       oacc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]}), pb, oacc[t], 0, 0, 0);
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");

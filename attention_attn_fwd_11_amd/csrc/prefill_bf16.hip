@@ -3,9 +3,9 @@
 // The tiled online-softmax loop of "GPU learning day 24: Operator Fusion",
 // section 3.4 (FlashAttention): a workgroup owns a block of query rows and
 // streams key/value blocks through LDS; per block it forms the scores on
-// chip, raises the running row max, rescales the running sum and the output
-// accumulator by exp(m_old - m_new), and adds exp(S - m_new) V.  One
-// division at the end.  The score matrix never leaves the chip.
+// chip, keeps a running row max and row sum, rescales the output
+// accumulator when the max moves, and adds exp(S - m) V.  One division at the
+// end.  The score matrix never leaves the chip.
 //
 // gfx950 design
 //   - 256 threads = 4 waves; each wave owns 32 query rows (128 per workgroup).
@@ -13,7 +13,7 @@
 //     K rows (from LDS) are the A operand and Q^T (held in registers for the
 //     whole loop) is the B operand.  In the accumulator each lane then holds
 //     one query column and 16 keys of it, so the row max and row sum are
-//     mostly lane-local; the two lane halves are joined with one exchange.
+//     lane-local apart from one exchange between the two lane halves.
 //   - The same accumulator, rounded to bf16, is directly the B operand of
 //     O^T += V^T P^T (the order of keys inside a 16-key step is permuted
 //     consistently on both operands, which leaves the sum unchanged).
@@ -21,15 +21,24 @@
 //     read (ds_read_b64_tr_b16), so V is never transposed in memory.
 //   - K/V blocks of 64 keys are double-buffered in LDS: the next block's
 //     global loads are issued before the current block's matrix work and
-//     written to the other buffer after it; one barrier per block.
+//     written to the other buffer after it; one barrier per block.  The loop
+//     is unrolled over the two buffers so every LDS address is a lane
+//     constant plus an immediate offset.
 //   - LDS rows are XOR-swizzled at 16-byte granularity so the row-parallel
 //     operand reads and the transpose reads are free of bank conflicts.
-//   - exp2 with log2(e) folded into the scale; P is rounded to bf16 before
-//     P V and the running sum is accumulated from the rounded values, so a
-//     constant V comes back exactly.
-//   - Causal tiles are launched heaviest first; a wave skips the matrix work
-//     of a block that lies wholly above its rows' diagonal, and masking is
-//     applied only on blocks that cross the diagonal or the length limit.
+//   - Softmax in base 2: the scale times log2(e) is folded into the FMA that
+//     forms the exponent; the block max is taken on raw scores (v_max3).
+//   - Lazy rescaling: the reference max of a row only moves when a block's
+//     max exceeds it by more than 2^8, so the accumulator is rescaled on a
+//     few blocks per row instead of every block.
+//   - P is rounded to bf16 before P V and the running sum is accumulated
+//     from the rounded values (v_dot2 with (1, 1)), so a constant V comes
+//     back exactly.
+//   - Masking code exists only on the path for blocks that cross the causal
+//     diagonal or the length limit; causal tiles are launched heaviest first
+//     and a wave skips the matrix work of a block wholly above its rows.
+#include <type_traits>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -40,29 +49,35 @@ namespace {
 constexpr int kRows = 128;   // query rows per workgroup
 constexpr int kKeys = 64;    // keys per LDS block
 constexpr int kThreads = 256;
+constexpr float kRescaleSlack = 8.f;   // base-2 headroom before the accumulator is rescaled
 
 template <int D>
 struct Tile {
   static constexpr int kSlots = D / 8;                    // 16-byte slots per row
-  static constexpr int kBytes = kKeys * D * 2;            // one K or V block
+  static constexpr int kRowBytes = D * 2;
+  static constexpr int kBytes = kKeys * kRowBytes;        // one K or V block
   static constexpr int kPiecesPerThread = kKeys * kSlots / kThreads;
   // byte offset of (row, 16-byte slot) inside a swizzled block
-  __device__ static __forceinline__ int off(int row, int slot) {
-    return (row * kSlots + (slot ^ (row % kSlots))) * 16;
+  __device__ static __forceinline__ uint32_t off(int row, int slot) {
+    return (uint32_t)(row * kSlots + (slot ^ (lds_swizzle(row) & (kSlots - 1)))) * 16u;
   }
 };
 
-template <int D, bool CAUSAL>
+// POS: the scale is >= 0, so the block extreme of the raw scores is their
+// max (a negative scale needs their min).
+template <int D, bool CAUSAL, bool POS>
 __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(PrefillParams p) {
   using T = Tile<D>;
   constexpr int KS = D / 16;       // k-steps of the score MFMA (16 features each)
   constexpr int DT = D / 32;       // 32-feature output tiles
   constexpr int NP = T::kPiecesPerThread;
 
-  __shared__ __attribute__((aligned(16))) unsigned char smem[2 * 2 * T::kBytes];
-  // stage s: K block at smem + s*kBytes, V block at smem + (2+s)*kBytes
-  auto kbuf = [&](int stage) { return smem + stage * T::kBytes; };
-  auto vbuf = [&](int stage) { return smem + (2 + stage) * T::kBytes; };
+  // Two stages of K and V blocks, as separate arrays so the compiler can see
+  // that filling one stage does not touch the stage being read.
+  __shared__ __attribute__((aligned(16))) unsigned char k_s0[T::kBytes];
+  __shared__ __attribute__((aligned(16))) unsigned char k_s1[T::kBytes];
+  __shared__ __attribute__((aligned(16))) unsigned char v_s0[T::kBytes];
+  __shared__ __attribute__((aligned(16))) unsigned char v_s1[T::kBytes];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -95,6 +110,8 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(PrefillParams
   int kend = n;
   if (CAUSAL) kend = min(n, max(0, last_row + n - p.Sq + 1));
   const int n_blocks = (kend + kKeys - 1) / kKeys;
+  const int wave_last_row = min(wave_row0 + 31, p.Sq - 1);
+  const int my_last = CAUSAL ? my_row + n - p.Sq : n - 1;   // last key this row sees
 
   // Q^T as the B operand: lane (col, half) holds Q[my_row][16*ks + 8*half .. +7].
   bf16x8 qreg[KS];
@@ -105,138 +122,190 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(PrefillParams
       qreg[ks] = as_bf16x8(ld16(qp + (int64_t)r * D + 16 * ks + 8 * half));
   }
 
+  // Staging by direct global -> LDS copies.  Copy u of wave w fills the
+  // 1 KiB LDS chunk c = u*4 + w of a block; lane i lands at byte 16*i of
+  // it, i.e. at (row, physical slot), and so fetches logical slot
+  // physical ^ swizzle(row) of that row.  Rows per pass are a multiple of 16,
+  // so the swizzle, and hence the lane's byte offset, only shift by a
+  // constant from one copy to the next.
+  constexpr int kPassBytes = kThreads * 16;                 // one copy round of all waves
+  const int st_byte0 = wave * 1024 + lane * 16;             // LDS byte of copy 0
+  const int st_row0 = st_byte0 / T::kRowBytes;
+  const int st_slot0 = (st_byte0 % T::kRowBytes) / 16 ^ (lds_swizzle(st_row0) & (T::kSlots - 1));
+  const uint32_t g_off0 = (uint32_t)(st_row0 * T::kRowBytes + st_slot0 * 16);
+  uint32_t k_off[KS];                       // K operand (row col; row col+32 adds a constant)
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) k_off[ks] = T::off(col, 2 * ks + half);
+  uint32_t v_lo[DT], v_hi[DT];              // V^T transpose reads for k-step 0
+  {
+    const int grp = lane >> 4, src = lane & 15;
+    const int r0 = 4 * (grp >> 1) + (src >> 2);
+#pragma unroll
+    for (int t = 0; t < DT; ++t) {
+      const int cidx = 32 * t + 16 * (grp & 1) + 4 * (src & 3);
+      v_lo[t] = T::off(r0, cidx >> 3) + (cidx & 7) * 2;
+      v_hi[t] = T::off(r0 + 8, cidx >> 3) + (cidx & 7) * 2;
+    }
+  }
+
   f32x16 oacc[DT];
 #pragma unroll
   for (int t = 0; t < DT; ++t) oacc[t] = f32x16{};
-  float m = kNegInf;      // running max (base-2 units) of this lane's query
+  float mref = kNegInf;   // reference max (base-2 units) of this lane's query
   float lsum = 0.f;       // this lane's share of the running sum
+  const float c = p.scale_log2;
+  constexpr float neutral = POS ? kNegInf : kPosInf;   // masked raw score
 
-  // Global -> register staging of one K/V block (rows clamped to n-1).
-  u32x4 kst[NP], vst[NP];
-  auto load_block = [&](int j0) {
-#pragma unroll
-    for (int u = 0; u < NP; ++u) {
-      const int piece = u * kThreads + tid;
-      const int row = piece / T::kSlots, slot = piece % T::kSlots;
-      const int64_t src = (int64_t)min(j0 + row, n - 1) * D + slot * 8;
-      kst[u] = ld16(kp + src);
-      vst[u] = ld16(vp + src);
-    }
+  auto kbuf = [&](auto stage_c) -> unsigned char* {
+    if constexpr (decltype(stage_c)::value == 0) return k_s0; else return k_s1;
   };
-  auto store_block = [&](int stage) {
-#pragma unroll
-    for (int u = 0; u < NP; ++u) {
-      const int piece = u * kThreads + tid;
-      const int row = piece / T::kSlots, slot = piece % T::kSlots;
-      *reinterpret_cast<u32x4*>(kbuf(stage) + T::off(row, slot)) = kst[u];
-      *reinterpret_cast<u32x4*>(vbuf(stage) + T::off(row, slot)) = vst[u];
-    }
+  auto vbuf = [&](auto stage_c) -> unsigned char* {
+    if constexpr (decltype(stage_c)::value == 0) return v_s0; else return v_s1;
   };
 
-  if (n_blocks > 0) {
-    load_block(0);
-    store_block(0);
-  }
-  __syncthreads();
-
-  for (int blk = 0; blk < n_blocks; ++blk) {
-    const int stage = blk & 1;
-    const int j0 = blk * kKeys;
-    const bool has_next = blk + 1 < n_blocks;
-    if (has_next) load_block(j0 + kKeys);
-
-    // Does any row of this wave see a key of this block?  (wave-uniform)
-    const int wave_last_row = min(wave_row0 + 31, p.Sq - 1);
-    const bool active = !CAUSAL || j0 <= wave_last_row + n - p.Sq;
-    if (active) {
-      const unsigned char* kb = kbuf(stage);
-      const unsigned char* vb = vbuf(stage);
-
-      // S^T = K Q^T for the two 32-key halves of the block.
-      f32x16 sacc[2];
+  // Copy one K/V block into LDS stage S.  Rows past n are clamped to row n-1
+  // (only on the last block) so no byte beyond a sequence is read.
+  auto load_block = [&](auto stage_c, int j0) {
+    unsigned char* kd = kbuf(stage_c) + wave * 1024;
+    unsigned char* vd = vbuf(stage_c) + wave * 1024;
+    if (j0 + kKeys <= n) {
+      const char* kb = reinterpret_cast<const char*>(kp + (int64_t)j0 * D);
+      const char* vb = reinterpret_cast<const char*>(vp + (int64_t)j0 * D);
 #pragma unroll
-      for (int sub = 0; sub < 2; ++sub) {
-        sacc[sub] = f32x16{};
-        const int krow = 32 * sub + col;
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          const bf16x8 a = as_bf16x8(*reinterpret_cast<const u32x4*>(kb + T::off(krow, 2 * ks + half)));
-          sacc[sub] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[ks], sacc[sub], 0, 0, 0);
-        }
+      for (int u = 0; u < NP; ++u) {
+        global_to_lds16(kb + g_off0 + u * kPassBytes, kd + u * kPassBytes);
+        global_to_lds16(vb + g_off0 + u * kPassBytes, vd + u * kPassBytes);
       }
-
-      // Scale to base-2 units and mask where the block crosses a limit.
-      const int wave_first_row = wave_row0;
-      const bool need_mask = (j0 + kKeys > n) ||
-                             (CAUSAL && j0 + kKeys - 1 > wave_first_row + n - p.Sq);
-      const int my_last = CAUSAL ? my_row + n - p.Sq : n - 1;
-      float tmax = kNegInf;
+    } else {
 #pragma unroll
-      for (int sub = 0; sub < 2; ++sub) {
+      for (int u = 0; u < NP; ++u) {
+        const int row = st_row0 + u * (kPassBytes / T::kRowBytes);
+        const int64_t src = (int64_t)min(j0 + row, n - 1) * T::kRowBytes + st_slot0 * 16;
+        global_to_lds16(reinterpret_cast<const char*>(kp) + src, kd + u * kPassBytes);
+        global_to_lds16(reinterpret_cast<const char*>(vp) + src, vd + u * kPassBytes);
+      }
+    }
+  };
+
+  // Softmax of one block's scores; MASKED selects the path with masking.
+  auto softmax = [&](auto masked_c, f32x16 (&sacc)[2], int j0, u32x4 (&pb)[4]) {
+    constexpr bool MASKED = decltype(masked_c)::value;
+    if (MASKED) {
+#pragma unroll
+      for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          float s = sacc[sub][i] * p.scale_log2;
-          if (need_mask) {
-            const int j = j0 + 32 * sub + 8 * (i / 4) + 4 * half + (i % 4);
-            if (j >= n || j > my_last) s = kNegInf;
-          }
-          sacc[sub][i] = s;
-          tmax = fmaxf(tmax, s);
+          const int j = j0 + 32 * sub + 8 * (i / 4) + 4 * half + (i % 4);
+          if (j >= n || j > my_last) sacc[sub][i] = neutral;
         }
-      }
-      tmax = fmaxf(tmax, shfl_xor(tmax, 32));
-      const float m_new = fmaxf(m, tmax);
-      const float m_use = m_new == kNegInf ? 0.f : m_new;
-      const float alpha = exp2_fast(m - m_use);
-      m = m_new;
-
-      // P = exp2(S - m), rounded to bf16; the running sum uses the rounded P.
-      u32x4 pb[4];
-      float psum = 0.f;
+    }
+    // Block extreme of the raw scores (max for a non-negative scale, min for
+    // a negative one), joined across the two lane halves.
+    float traw = sacc[0][0];
+    if (POS) {
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        uint32_t w[4];
+      for (int i = 1; i < 32; ++i) traw = fmaxf(traw, sacc[i / 16][i % 16]);
+      traw = max_across_halves(traw);
+    } else {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int i0 = 8 * (c % 2) + 2 * e;
-          const float p0 = exp2_fast(sacc[c / 2][i0] - m_use);
-          const float p1 = exp2_fast(sacc[c / 2][i0 + 1] - m_use);
-          w[e] = pack_bf16x2(p0, p1);
-          psum += bf16_lo(w[e]) + bf16_hi(w[e]);
-        }
-        pb[c] = u32x4{w[0], w[1], w[2], w[3]};
-      }
-      lsum = lsum * alpha + psum;
+      for (int i = 1; i < 32; ++i) traw = fminf(traw, sacc[i / 16][i % 16]);
+      traw = min_across_halves(traw);
+    }
+    const float tmax = (MASKED && traw == neutral) ? kNegInf : traw * c;
+    const float cand = fmaxf(mref, tmax);
+    if (__any(cand > mref + kRescaleSlack)) {
+      const float alpha = cand == kNegInf ? 1.f : exp2_fast(mref - cand);
+      mref = cand;
+      lsum *= alpha;
 #pragma unroll
       for (int t = 0; t < DT; ++t) oacc[t] *= alpha;
-
-      // O^T += V^T P^T; V^T comes from transpose reads of the row-major block.
-      const int grp = lane >> 4;          // 16-lane group
-      const int src = lane & 15;          // source lane within the group
-      const int khalf = grp >> 1;         // = half
+    }
+    const float negm = -mref;
+    float psum = 0.f;
 #pragma unroll
-      for (int t = 0; t < DT; ++t) {
-        const int d0 = 32 * t + 16 * (grp & 1);
-        const int cidx = d0 + 4 * (src & 3);           // column this lane addresses
-        const int cslot = cidx >> 3, cbyte = (cidx & 7) * 2;
+    for (int cc = 0; cc < 4; ++cc) {
+      uint32_t w[4];
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          const int r0 = 16 * c + 4 * khalf + (src >> 2);
-          const int r1 = r0 + 8;
-          const u32x2 lo = lds_read_tr16x4(vb + T::off(r0, cslot) + cbyte);
-          const u32x2 hi = lds_read_tr16x4(vb + T::off(r1, cslot) + cbyte);
-          const bf16x8 a = as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]});
-          oacc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, as_bf16x8(pb[c]), oacc[t], 0, 0, 0);
+      for (int e = 0; e < 4; ++e) {
+        const int i0 = 8 * (cc % 2) + 2 * e;
+        const float s0 = sacc[cc / 2][i0], s1 = sacc[cc / 2][i0 + 1];
+        float p0 = exp2_fast(fmaf(s0, c, negm));
+        float p1 = exp2_fast(fmaf(s1, c, negm));
+        if (MASKED) {
+          p0 = s0 == neutral ? 0.f : p0;
+          p1 = s1 == neutral ? 0.f : p1;
         }
+        w[e] = pack_bf16x2(p0, p1);
+        psum = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(w[e]), kOnesBf16x2, psum, false);
+      }
+      pb[cc] = u32x4{w[0], w[1], w[2], w[3]};
+    }
+    lsum += psum;
+  };
+
+  // One block of keys from LDS buffer S.
+  auto compute_block = [&](auto stage_c, int j0) {
+    constexpr int S = decltype(stage_c)::value;
+    const unsigned char* kb = kbuf(stage_c);
+    const unsigned char* vb = vbuf(stage_c);
+
+    // S^T = K Q^T for the two 32-key halves of the block.
+    // (the two accumulation chains are interleaved so consecutive MFMAs are
+    // independent)
+    f32x16 sacc[2] = {f32x16{}, f32x16{}};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll
+      for (int sub = 0; sub < 2; ++sub) {
+        const bf16x8 a = as_bf16x8(*reinterpret_cast<const u32x4*>(
+            kb + sub * 32 * T::kRowBytes + k_off[ks]));
+        sacc[sub] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[ks], sacc[sub], 0, 0, 0);
       }
     }
 
-    if (has_next) store_block(stage ^ 1);
-    __syncthreads();
+    u32x4 pb[4];
+    const bool need_mask = (j0 + kKeys > n) ||
+                           (CAUSAL && j0 + kKeys - 1 > wave_row0 + n - p.Sq);
+    if (need_mask)
+      softmax(std::true_type{}, sacc, j0, pb);
+    else
+      softmax(std::false_type{}, sacc, j0, pb);
+
+    // O^T += V^T P^T; V^T comes from transpose reads of the row-major block.
+    // (k-step outer, output tile inner: DT independent accumulation chains)
+#pragma unroll
+    for (int cc = 0; cc < 4; ++cc) {
+#pragma unroll
+      for (int t = 0; t < DT; ++t) {
+        const u32x2 lo = lds_read_tr16x4(vb + cc * 16 * T::kRowBytes + v_lo[t]);
+        const u32x2 hi = lds_read_tr16x4(vb + cc * 16 * T::kRowBytes + v_hi[t]);
+        const bf16x8 a = as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]});
+        oacc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, as_bf16x8(pb[cc]), oacc[t], 0, 0, 0);
+      }
+    }
+  };
+
+  auto step = [&](auto stage_c, int blk) {
+    constexpr int S = decltype(stage_c)::value;
+    const int j0 = blk * kKeys;
+    // The other stage was last read in the previous step, before its barrier.
+    if (blk + 1 < n_blocks) load_block(std::integral_constant<int, 1 - S>{}, j0 + kKeys);
+    // Does any row of this wave see a key of this block?  (wave-uniform)
+    if (!CAUSAL || j0 <= wave_last_row + n - p.Sq) compute_block(stage_c, j0);
+    wait_vmem();        // this wave's copies of the next block have landed
+    __syncthreads();    // ... and every other wave's
+  };
+
+  if (n_blocks > 0) load_block(std::integral_constant<int, 0>{}, 0);
+  wait_vmem();
+  __syncthreads();
+  for (int blk = 0; blk < n_blocks; blk += 2) {
+    step(std::integral_constant<int, 0>{}, blk);
+    if (blk + 1 < n_blocks) step(std::integral_constant<int, 1>{}, blk + 1);
   }
 
   // Epilogue: O = O_acc / l, rounded to bf16.
-  const float l = lsum + shfl_xor(lsum, 32);
+  const float l = sum_across_halves(lsum);
   const float inv = l > 0.f ? 1.f / l : 0.f;
   if (my_row < p.Sq) {
     uint16_t* orow = op + (int64_t)my_row * D;
@@ -257,7 +326,10 @@ template <int D, bool CAUSAL>
 hipError_t launch(const PrefillParams& p, hipStream_t stream) {
   const int n_qt = (p.Sq + kRows - 1) / kRows;
   dim3 grid((unsigned)n_qt * p.Hq * p.B);
-  hipLaunchKernelGGL((prefill_bf16_kernel<D, CAUSAL>), grid, dim3(kThreads), 0, stream, p);
+  if (p.scale_log2 >= 0.f)
+    hipLaunchKernelGGL((prefill_bf16_kernel<D, CAUSAL, true>), grid, dim3(kThreads), 0, stream, p);
+  else
+    hipLaunchKernelGGL((prefill_bf16_kernel<D, CAUSAL, false>), grid, dim3(kThreads), 0, stream, p);
   return hipGetLastError();
 }
 

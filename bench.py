@@ -43,6 +43,8 @@ def parse():
                     help="time only the headline step (prefill + MHA decode)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time for the oracle sample")
+    ap.add_argument("--only", default=None,
+                    help="time one named workload only and print its line (for profiling)")
     return ap.parse_args()
 
 
@@ -98,6 +100,33 @@ def cpu_baseline(w, x, seconds):
     }
 
 
+def only(args, torch, attn, wl, dev):
+    """Warm up and time one workload (nothing else launched in between)."""
+    w = wl.BY_NAME[args.only]
+    x = wl.generate(w, dev)
+    o = torch.empty_like(x["q"])
+    if w.kind == "prefill":
+        f = lambda: attn.prefill(x["q"], x["k"], x["v"], causal=w.causal, scale=w.scale, out=o)
+        work, unit = wl.prefill_flops(w), "TFLOP/s"
+    else:
+        f = lambda: attn.decode(x["q"], x["k"], x["v"], kv_lens=x["kv_lens"], scale=w.scale, out=o)
+        work, unit = wl.decode_kv_bytes(w, x["kv_lens"].cpu()), "GB/s"
+    for _ in range(args.warmup):
+        f()
+    torch.cuda.synchronize()
+    tm = Timer(torch)
+    for _ in range(args.steps):
+        tm(f)
+    torch.cuda.synchronize()
+    ms, all_ms = tm.mean_ms()
+    rate = work / (ms * 1e-3) / (1e12 if unit == "TFLOP/s" else 1e9)
+    peak = PEAK_BF16_TFLOPS if unit == "TFLOP/s" else PEAK_HBM_GBPS
+    print(json.dumps({"workload": w.name, "shape": w.describe(), "ms": round(ms, 4),
+                      "min_ms": round(min(all_ms), 4), "max_ms": round(max(all_ms), 4),
+                      "rate": round(rate, 2), "unit": unit, "frac": round(rate / peak, 4),
+                      "steps": args.steps, "warmup": args.warmup}), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -114,6 +143,8 @@ def main():
         sys.exit(1)
     dev = "cuda:0"
     torch.cuda.set_device(0)
+    if args.only:
+        return only(args, torch, attn, wl, dev)
 
     wp = wl.BY_NAME["prefill_bf16_b4h32s4096"]
     wd = wl.BY_NAME["decode_bf16_b64h32l4096"]
