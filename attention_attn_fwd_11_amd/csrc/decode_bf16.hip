@@ -213,7 +213,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_valu(DecodeParams p) {
 // inside the loop.
 // ---------------------------------------------------------------------------
 template <int D, int G>
-__global__ __launch_bounds__(kThreads) void decode_split_mfma(DecodeParams p) {
+__global__ __launch_bounds__(kThreads, 3) void decode_split_mfma(DecodeParams p) {
   constexpr int KS = D / 32;          // k-steps of the score MFMA (32 features each)
   constexpr int DT = D / 16;          // 16-feature output tiles
   constexpr int SLOTS = D / 8;        // 16-byte slots per V row
@@ -257,24 +257,38 @@ __global__ __launch_bounds__(kThreads) void decode_split_mfma(DecodeParams p) {
   for (int t = 0; t < DT; ++t) oacc[t] = f32x4{};
   float m = kNegInf, lsum = 0.f;
   unsigned char* vb = vbuf[wave];
+  const uint32_t k_off = (uint32_t)(qcol * D * 2 + grp * 16);   // byte offset of this lane's K piece
 
   for (int base = c0 + wave * 32; base < c1; base += kWaves * 32) {
     // K as A operand: lane (row = lane%16, grp) -> K[base + 16*hlf + row][32*ks + 8*grp ..]
-    u32x4 kr[2][KS];
-#pragma unroll
-    for (int hlf = 0; hlf < 2; ++hlf) {
-      const int key = min(base + 16 * hlf + qcol, c1 - 1);
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) kr[hlf][ks] = ld16(kp + (int64_t)key * D + 32 * ks + 8 * grp);
-    }
     // V rows of this step: coalesced pieces, row = piece / SLOTS.
+    // A full step reads from a uniform base plus lane-constant offsets; the
+    // last, partial step clamps rows to the chunk's last valid key.
+    u32x4 kr[2][KS];
     u32x4 vr[VP];
+    if (base + 32 <= c1) {
+      const char* kb = reinterpret_cast<const char*>(kp + (int64_t)base * D);
+      const char* vbs = reinterpret_cast<const char*>(vp + (int64_t)base * D);
 #pragma unroll
-    for (int u = 0; u < VP; ++u) {
-      const int piece = u * 64 + lane;
-      const int row = piece / SLOTS, slot = piece % SLOTS;
-      const int key = min(base + row, c1 - 1);
-      vr[u] = ld16(vp + (int64_t)key * D + slot * 8);
+      for (int hlf = 0; hlf < 2; ++hlf)
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) kr[hlf][ks] = ld16(kb + k_off + hlf * 16 * D * 2 + ks * 64);
+#pragma unroll
+      for (int u = 0; u < VP; ++u) vr[u] = ld16(vbs + lane * 16 + u * 1024);
+    } else {
+#pragma unroll
+      for (int hlf = 0; hlf < 2; ++hlf) {
+        const int key = min(base + 16 * hlf + qcol, c1 - 1);
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) kr[hlf][ks] = ld16(kp + (int64_t)key * D + 32 * ks + 8 * grp);
+      }
+#pragma unroll
+      for (int u = 0; u < VP; ++u) {
+        const int piece = u * 64 + lane;
+        const int row = piece / SLOTS, slot = piece % SLOTS;
+        const int key = min(base + row, c1 - 1);
+        vr[u] = ld16(vp + (int64_t)key * D + slot * 8);
+      }
     }
     // S^T for keys [base, base+16) and [base+16, base+32)
     f32x4 sacc[2];
