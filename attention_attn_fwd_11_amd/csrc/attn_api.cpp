@@ -9,6 +9,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 
 #include "kernels.hpp"
 
@@ -45,9 +46,19 @@ attn_status_t check_common(const void* q, const void* k, const void* v, const vo
   return ATTN_OK;
 }
 
-// Keys per decode split.  Test-only override: ATTN_DECODE_CHUNK (a positive
-// multiple of 256) forces the chunk so split-count invariance can be tested.
-int decode_chunk(int32_t B, int32_t H_kv, int32_t S_kv) {
+// Decode work decomposition.  Query groups (G >= 2) with at most
+// kDecodeMaxBatch sequences use the balanced pass: fixed units of
+// kDecodeUnit keys spread evenly over a persistent grid.  Otherwise the cache
+// is split into equal chunks per (batch, head).
+bool decode_balanced(int32_t B, int32_t H_q, int32_t H_kv) {
+  return H_q / H_kv >= 2 && B <= attn::kDecodeMaxBatch;
+}
+
+// Keys per split (or per unit on the balanced pass).  Test-only override for
+// the chunked pass: ATTN_DECODE_CHUNK (a positive multiple of 256) forces the
+// chunk so split-count invariance can be tested.
+int decode_chunk(int32_t B, int32_t H_q, int32_t H_kv, int32_t S_kv) {
+  if (decode_balanced(B, H_q, H_kv)) return attn::kDecodeUnit;
   if (const char* env = std::getenv("ATTN_DECODE_CHUNK")) {
     const long c = std::strtol(env, nullptr, 10);
     if (c >= 256 && c % 256 == 0 && c <= (1 << 30)) return (int)c;
@@ -64,6 +75,24 @@ int decode_chunk(int32_t B, int32_t H_kv, int32_t S_kv) {
   chunk = (chunk + 255) / 256 * 256;
   if (chunk < 256) chunk = 256;
   return (int)chunk;
+}
+
+// Compute units of the current device, queried once per device.
+int device_cus(int* dev_out) {
+  static std::mutex mu;
+  static int cus[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return -1;
+  *dev_out = dev;
+  if (dev < 0 || dev >= 64) return -1;
+  std::lock_guard<std::mutex> lock(mu);
+  if (cus[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      return -1;
+    cus[dev] = n;
+  }
+  return cus[dev];
 }
 
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
@@ -91,7 +120,7 @@ const char* attn_last_hip_error(void) { return g_hip_error; }
 size_t attn_decode_workspace_bytes(int32_t B, int32_t H_q, int32_t H_kv, int32_t S_kv, int32_t d) {
   if (B <= 0 || S_kv <= 0 || H_q < 1 || H_kv < 1 || H_q % H_kv != 0 || (d != 64 && d != 128))
     return 0;
-  const int chunk = decode_chunk(B, H_kv, S_kv);
+  const int chunk = decode_chunk(B, H_q, H_kv, S_kv);
   const int64_t n_split = (S_kv + chunk - 1) / chunk;
   const size_t rows = (size_t)B * H_q * n_split;
   return round_up(rows * d * sizeof(float), 256) + round_up(rows * sizeof(float), 256);
@@ -147,8 +176,24 @@ attn_status_t attn_decode_fwd(const void* q, const void* k_cache, const void* v_
   attn::DecodeParams p{};
   p.q = q; p.k = k_cache; p.v = v_cache; p.o = o; p.kv_lens = kv_lens;
   p.B = B; p.Hq = H_q; p.Hkv = H_kv; p.Skv = S_kv; p.d = d;
-  p.chunk = decode_chunk(B, H_kv, S_kv);
+  p.chunk = decode_chunk(B, H_q, H_kv, S_kv);
   p.n_split = (S_kv + p.chunk - 1) / p.chunk;
+  p.n_wg = 0;
+  if (decode_balanced(B, H_q, H_kv)) {
+    // Persistent grid: three resident workgroups per compute unit, never more
+    // than there are units.  Test-only override: ATTN_DECODE_WORKGROUPS.
+    int dev = 0;
+    const int cus = device_cus(&dev);
+    if (cus <= 0) return hip_fail("hipDeviceGetAttribute(multiprocessor count)", hipGetLastError());
+    int64_t wg = 3 * (int64_t)cus;
+    if (const char* env = std::getenv("ATTN_DECODE_WORKGROUPS")) {
+      const long w = std::strtol(env, nullptr, 10);
+      if (w >= 1 && w <= (1 << 20)) wg = w;
+    }
+    const int64_t max_units = (int64_t)B * H_kv * p.n_split;
+    if (wg > max_units) wg = max_units;
+    p.n_wg = (int)wg;
+  }
   const size_t rows = (size_t)B * H_q * p.n_split;
   p.part_o = static_cast<float*>(workspace);
   p.part_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) +

@@ -391,6 +391,311 @@ __global__ __launch_bounds__(kThreads, 3) void decode_split_mfma(DecodeParams p)
 }
 
 // ---------------------------------------------------------------------------
+// G >= 2, balanced: a persistent split pass over equal-size work units.
+//
+// With ragged lengths a grid of (split, head, batch) workgroups leaves many
+// compute units idle at the end (short and empty splits).  Here the cache is
+// cut into units of kDecodeUnit keys, ordered (batch, KV head, unit); unit
+// counts per batch come from the lengths on the device, and every workgroup
+// recomputes their prefix sum in LDS.  Workgroup w takes units
+// [w*R, (w+1)*R), R = ceil(U / gridDim.x), walking across heads: runs of units
+// of one head are merged on the fly, and each run ("segment") leaves one
+// partial (o, base-2 lse) per query head, stored at the slot of the
+// segment's first unit.  The combine kernel finds a head's segments from the
+// same prefix sums and R.
+// ---------------------------------------------------------------------------
+
+// Exclusive prefix over batches of H_kv * ceil(n_b / kDecodeUnit) into pre[0..B]
+// (pre[B] = total units).  All threads of the workgroup take part.
+__device__ __forceinline__ void unit_prefix(const DecodeParams& p, int* pre, int* wave_tot) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int per = (p.B + kThreads - 1) / kThreads;      // batches per thread (<= 8)
+  const int b0 = tid * per;
+  int vals[kDecodeMaxBatch / kThreads];
+  int sum = 0;
+#pragma unroll
+  for (int i = 0; i < kDecodeMaxBatch / kThreads; ++i) {
+    int u = 0;
+    if (i < per && b0 + i < p.B) {
+      int n = p.Skv;
+      if (p.kv_lens) n = min(max(p.kv_lens[b0 + i], 0), p.Skv);
+      u = p.Hkv * ((n + kDecodeUnit - 1) / kDecodeUnit);
+    }
+    vals[i] = u;
+    sum += u;
+  }
+  // inclusive scan of the per-thread sums within the wave
+  int incl = sum;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int t = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += t;
+  }
+  if (lane == 63) wave_tot[wave] = incl;
+  __syncthreads();
+  int base = 0;
+  for (int w = 0; w < wave; ++w) base += wave_tot[w];
+  int run = base + incl - sum;                         // exclusive prefix of this thread
+#pragma unroll
+  for (int i = 0; i < kDecodeMaxBatch / kThreads; ++i) {
+    if (i < per && b0 + i < p.B) pre[b0 + i] = run;
+    run += vals[i];
+  }
+  if (tid == kThreads - 1) pre[p.B] = base + incl;
+  __syncthreads();
+}
+
+template <int D, int G>
+__global__ __launch_bounds__(kThreads, 3) void decode_split_balanced(DecodeParams p) {
+  constexpr int KS = D / 32;          // k-steps of the score MFMA (32 features each)
+  constexpr int DT = D / 16;          // 16-feature output tiles
+  constexpr int SLOTS = D / 8;        // 16-byte slots per V row
+  constexpr int VBYTES = 32 * D * 2;  // one wave's V block
+  constexpr int VP = 32 * SLOTS / 64; // V pieces per lane per step
+
+  static_assert(kWaves * G * D * 4 <= kWaves * VBYTES, "merge buffer must fit the V buffers");
+  __shared__ __attribute__((aligned(16))) unsigned char vbuf[kWaves][VBYTES];
+  __shared__ float mrg_m[kWaves][16];
+  __shared__ float mrg_l[kWaves][16];
+  __shared__ int pre[kDecodeMaxBatch + 1];
+  __shared__ int wave_tot[kWaves];
+  float (*mrg_o)[G][D] = reinterpret_cast<float (*)[G][D]>(&vbuf[0][0]);
+
+  unit_prefix(p, pre, wave_tot);
+  const int U = pre[p.B];
+  const int R = (U + (int)gridDim.x - 1) / (int)gridDim.x;
+  int u = (int)blockIdx.x * R;
+  const int uend = min(u + R, U);
+  if (u >= uend) return;                               // uniform across the workgroup
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int qcol = lane & 15;          // query column (valid if < G)
+  const int grp = lane >> 4;           // 16-lane group
+  unsigned char* vb = vbuf[wave];
+  const uint32_t k_off = (uint32_t)(qcol * D * 2 + grp * 16);   // byte offset of this lane's K piece
+  // V copy w puts this lane's 16 bytes at LDS row v_row0 + w*kRowsPerCopy,
+  // physical slot v_phys; the swizzle of that row picks the logical slot.
+  constexpr int kRowsPerCopy = 1024 / (2 * D);
+  const int v_row0 = (lane * 16) / (2 * D);
+  const int v_phys = ((lane * 16) % (2 * D)) / 16;
+  auto v_slot = [&](int w) {
+    return v_phys ^ (lds_swizzle(v_row0 + w * kRowsPerCopy) & (SLOTS - 1));
+  };
+
+  // Locate unit u: batch b = last with pre[b] <= u (batches without units
+  // have pre[b] == pre[b+1] and are skipped by taking the last such b).
+  int lo = 0, hi = p.B - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (pre[mid] <= u) lo = mid; else hi = mid - 1;
+  }
+  int b = lo;
+  int units_b = (pre[b + 1] - pre[b]) / p.Hkv;
+  int hk = (u - pre[b]) / units_b;
+  int k = (u - pre[b]) % units_b;
+
+  while (u < uend) {
+    int n = p.Skv;
+    if (p.kv_lens) n = min(max(p.kv_lens[b], 0), p.Skv);
+    const int seg_start = u;
+    const int seg_end = min(uend, pre[b] + (hk + 1) * units_b);
+    const uint16_t* kp = static_cast<const uint16_t*>(p.k) + ((int64_t)b * p.Hkv + hk) * p.Skv * D;
+    const uint16_t* vp = static_cast<const uint16_t*>(p.v) + ((int64_t)b * p.Hkv + hk) * p.Skv * D;
+
+    // Q^T as B operand: lane (qcol, grp) holds Q[h0 + qcol][32*ks + 8*grp .. +7].
+    bf16x8 qreg[KS];
+    {
+      const uint16_t* qp = static_cast<const uint16_t*>(p.q) + ((int64_t)b * p.Hq + (int64_t)hk * G) * D;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        u32x4 w = {0u, 0u, 0u, 0u};
+        if (qcol < G) w = ld16(qp + (int64_t)qcol * D + 32 * ks + 8 * grp);
+        qreg[ks] = as_bf16x8(w);
+      }
+    }
+    f32x4 oacc[DT];
+#pragma unroll
+    for (int t = 0; t < DT; ++t) oacc[t] = f32x4{};
+    float m = kNegInf, lsum = 0.f;
+
+    for (; u < seg_end; ++u, ++k) {
+      const int base = k * kDecodeUnit + wave * 32;
+      if (base >= n) continue;                         // this wave's slice is past the length
+      // K into registers (A-operand layout); V straight into this wave's LDS
+      // region by direct copies (copy w lands lane i at byte w*1024 + 16*i).
+      u32x4 kr[2][KS];
+      if (base + 32 <= n) {
+        const char* kb = reinterpret_cast<const char*>(kp + (int64_t)base * D);
+        const char* vbs = reinterpret_cast<const char*>(vp + (int64_t)base * D);
+#pragma unroll
+        for (int hlf = 0; hlf < 2; ++hlf)
+#pragma unroll
+          for (int ks = 0; ks < KS; ++ks) kr[hlf][ks] = ld16(kb + k_off + hlf * 16 * D * 2 + ks * 64);
+#pragma unroll
+        for (int w = 0; w < VP; ++w)
+          global_to_lds16(vbs + (v_row0 + w * kRowsPerCopy) * 2 * D + v_slot(w) * 16, vb + w * 1024);
+      } else {
+#pragma unroll
+        for (int hlf = 0; hlf < 2; ++hlf) {
+          const int key = min(base + 16 * hlf + qcol, n - 1);
+#pragma unroll
+          for (int ks = 0; ks < KS; ++ks) kr[hlf][ks] = ld16(kp + (int64_t)key * D + 32 * ks + 8 * grp);
+        }
+#pragma unroll
+        for (int w = 0; w < VP; ++w) {
+          const int key = min(base + v_row0 + w * kRowsPerCopy, n - 1);
+          global_to_lds16(reinterpret_cast<const char*>(vp + (int64_t)key * D) + v_slot(w) * 16,
+                          vb + w * 1024);
+        }
+      }
+      f32x4 sacc[2];
+#pragma unroll
+      for (int hlf = 0; hlf < 2; ++hlf) {
+        sacc[hlf] = f32x4{};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+          sacc[hlf] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kr[hlf][ks]), qreg[ks], sacc[hlf], 0, 0, 0);
+      }
+      // lane holds keys base + 16*hlf + 4*grp + i for query qcol
+      float tmax = kNegInf;
+#pragma unroll
+      for (int hlf = 0; hlf < 2; ++hlf)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int key = base + 16 * hlf + 4 * grp + i;
+          const float s = key < n ? sacc[hlf][i] * p.scale_log2 : kNegInf;
+          sacc[hlf][i] = s;
+          tmax = fmaxf(tmax, s);
+        }
+      tmax = fmaxf(tmax, shfl_xor(tmax, 16));
+      tmax = fmaxf(tmax, shfl_xor(tmax, 32));
+      const float m_new = fmaxf(m, tmax);            // finite: the slice has a valid key
+      const float alpha = exp2_fast(m - m_new);
+      m = m_new;
+      uint32_t pw[4];
+      float psum = 0.f;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int hlf = e / 2, i0 = 2 * (e % 2);
+        pw[e] = pack_bf16x2(exp2_fast(sacc[hlf][i0] - m_new), exp2_fast(sacc[hlf][i0 + 1] - m_new));
+        psum = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(pw[e]), kOnesBf16x2, psum, false);
+      }
+      lsum = lsum * alpha + psum;
+      const bf16x8 pb = as_bf16x8(u32x4{pw[0], pw[1], pw[2], pw[3]});
+#pragma unroll
+      for (int t = 0; t < DT; ++t) oacc[t] *= alpha;
+
+      wait_vmem();       // this wave's V copies have landed in its LDS region
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      const int src = lane & 15;
+#pragma unroll
+      for (int t = 0; t < DT; ++t) {
+        const int cidx = 16 * t + 4 * (src & 3);
+        const int cslot = cidx >> 3, cbyte = (cidx & 7) * 2;
+        const int r0 = 4 * grp + (src >> 2);
+        const int r1 = r0 + 16;
+        const u32x2 lo2 = lds_read_tr16x4(vb + (r0 * SLOTS + (cslot ^ (lds_swizzle(r0) & (SLOTS - 1)))) * 16 + cbyte);
+        const u32x2 hi2 = lds_read_tr16x4(vb + (r1 * SLOTS + (cslot ^ (lds_swizzle(r1) & (SLOTS - 1)))) * 16 + cbyte);
+        oacc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(u32x4{lo2[0], lo2[1], hi2[0], hi2[1]}), pb, oacc[t], 0, 0, 0);
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    }
+
+    // Flush the segment: merge the waves, write one partial per query head.
+    lsum += shfl_xor(lsum, 16);
+    lsum += shfl_xor(lsum, 32);
+    if (lane < 16) {
+      mrg_m[wave][qcol] = m;
+      mrg_l[wave][qcol] = lsum;
+    }
+    __syncthreads();   // every wave is done with its V buffer before it is reused
+    if (qcol < G) {
+#pragma unroll
+      for (int t = 0; t < DT; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) mrg_o[wave][qcol][16 * t + 4 * grp + i] = oacc[t][i];
+    }
+    __syncthreads();
+    for (int idx = tid; idx < G * D; idx += kThreads) {
+      const int qi = idx / D, d = idx % D;
+      float M = kNegInf;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) M = fmaxf(M, mrg_m[w][qi]);
+      float L = 0.f, acc = 0.f;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) {
+        const float wt = mrg_m[w][qi] == kNegInf ? 0.f : exp2_fast(mrg_m[w][qi] - M);
+        L += wt * mrg_l[w][qi];
+        acc += wt * mrg_o[w][qi][d];
+      }
+      const int64_t slot = (int64_t)seg_start * G + qi;
+      p.part_o[slot * D + d] = acc / L;
+      if (d == 0) p.part_lse[slot] = M + log2_fast(L);
+    }
+    __syncthreads();   // the merge buffer (aliasing the V buffers) is free again
+
+    // next head: skip batches without units
+    k = 0;
+    if (++hk == p.Hkv) {
+      hk = 0;
+      do { ++b; } while (b < p.B && pre[b + 1] == pre[b]);
+      if (b < p.B) units_b = (pre[b + 1] - pre[b]) / p.Hkv;
+    }
+  }
+}
+
+// Combine for the balanced pass: head (b, g) owns units [hs, he); its
+// segments start at hs and at every multiple of R inside (hs, he).
+template <int D, int G>
+__global__ __launch_bounds__(64) void decode_combine_balanced(DecodeParams p) {
+  const int hq = blockIdx.x, b = blockIdx.y;
+  const int lane = threadIdx.x;
+  const int g = hq / G, qi = hq % G;
+  // units before batch b, and in total (lane-strided sums over batches)
+  int before = 0, total = 0, units_b = 0;
+  for (int bb = lane; bb < p.B; bb += 64) {
+    int n = p.Skv;
+    if (p.kv_lens) n = min(max(p.kv_lens[bb], 0), p.Skv);
+    const int ub = (n + kDecodeUnit - 1) / kDecodeUnit;
+    total += ub;
+    if (bb < b) before += ub;
+    if (bb == b) units_b = ub;
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    before += __shfl_xor(before, o, 64);
+    total += __shfl_xor(total, o, 64);
+    units_b += __shfl_xor(units_b, o, 64);
+  }
+  const int U = total * p.Hkv;
+  const int R = (U + p.n_wg - 1) / p.n_wg;
+  const int hs = before * p.Hkv + g * units_b, he = hs + units_b;
+  uint16_t* orow = static_cast<uint16_t*>(p.o) + ((int64_t)b * p.Hq + hq) * D;
+  constexpr int PER = D / 64;
+  float acc[PER];
+#pragma unroll
+  for (int e = 0; e < PER; ++e) acc[e] = 0.f;
+  float M = kNegInf;
+  for (int s = hs; s < he; s = (s / R + 1) * R) M = fmaxf(M, p.part_lse[(int64_t)s * G + qi]);
+  float Wsum = 0.f;
+  for (int s = hs; s < he; s = (s / R + 1) * R) {
+    const int64_t slot = (int64_t)s * G + qi;
+    const float wt = exp2_fast(p.part_lse[slot] - M);
+    Wsum += wt;
+#pragma unroll
+    for (int e = 0; e < PER; ++e) acc[e] = fmaf(wt, p.part_o[slot * D + PER * lane + e], acc[e]);
+  }
+  const float inv = he > hs ? 1.f / Wsum : 0.f;
+  if (PER == 2) {
+    reinterpret_cast<uint32_t*>(orow)[lane] = pack_bf16x2(acc[0] * inv, acc[PER - 1] * inv);
+  } else {
+    orow[lane] = f32_to_bf16_bits(acc[0] * inv);
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Combine: O = sum_s 2^(lse_s - M) o_s / sum_s 2^(lse_s - M), M = max_s lse_s.
 // ---------------------------------------------------------------------------
 template <int D>
@@ -423,9 +728,27 @@ __global__ __launch_bounds__(64) void decode_combine(DecodeParams p) {
   }
 }
 
+template <int D, int G>
+hipError_t launch_balanced(const DecodeParams& p, hipStream_t stream) {
+  hipLaunchKernelGGL((decode_split_balanced<D, G>), dim3(p.n_wg), dim3(kThreads), 0, stream, p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((decode_combine_balanced<D, G>), dim3(p.Hq, p.B), dim3(64), 0, stream, p);
+  return hipGetLastError();
+}
+
 template <int D>
 hipError_t launch_d(const DecodeParams& p, hipStream_t stream) {
   const int G = p.Hq / p.Hkv;
+  if (p.n_wg > 0) {
+    switch (G) {
+      case 2: return launch_balanced<D, 2>(p, stream);
+      case 4: return launch_balanced<D, 4>(p, stream);
+      case 8: return launch_balanced<D, 8>(p, stream);
+      case 16: return launch_balanced<D, 16>(p, stream);
+      default: return hipErrorInvalidValue;
+    }
+  }
   dim3 grid(p.n_split, p.Hkv, p.B);
   switch (G) {
     case 1: hipLaunchKernelGGL((decode_split_valu<D>), grid, dim3(kThreads), 0, stream, p); break;

@@ -29,10 +29,17 @@ struct DecodeParams {
   float* part_o;           // [B, Hq, n_split, d] fp32
   float* part_lse;         // [B, Hq, n_split]   fp32, base-2 log-sum-exp
   int B, Hq, Hkv, Skv, d;
-  int chunk;               // keys per split (multiple of 256)
-  int n_split;
+  int chunk;               // keys per split (G = 1) or per unit (G >= 2)
+  int n_split;             // partial slots per (batch, query head)
+  int n_wg;                // G >= 2: workgroups of the balanced split pass
   float scale_log2;
 };
+
+// Largest batch the balanced (G >= 2) decode pass handles: its workgroups
+// keep a prefix sum of per-batch work in LDS.
+constexpr int kDecodeMaxBatch = 2048;
+// Keys per work unit of the balanced decode pass (4 waves x 32 keys).
+constexpr int kDecodeUnit = 128;
 
 hipError_t launch_prefill_f32(const PrefillParams& p, hipStream_t stream);
 hipError_t launch_prefill_bf16(const PrefillParams& p, hipStream_t stream);

@@ -163,32 +163,48 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(PrefillParams
     if constexpr (decltype(stage_c)::value == 0) return v_s0; else return v_s1;
   };
 
-  // Copy one K/V block into LDS stage S.  Rows past n are clamped to row n-1
-  // (only on the last block) so no byte beyond a sequence is read.
-  auto load_block = [&](auto stage_c, int j0) {
-    unsigned char* kd = kbuf(stage_c) + wave * 1024;
-    unsigned char* vd = vbuf(stage_c) + wave * 1024;
+  // Copy one K (or V) block into LDS stage S.  Rows past n are clamped to
+  // row n-1 (only on the last block) so no byte beyond a sequence is read.
+  auto copy_block = [&](const uint16_t* src, unsigned char* dst, int j0) {
+    unsigned char* d = dst + wave * 1024;
     if (j0 + kKeys <= n) {
-      const char* kb = reinterpret_cast<const char*>(kp + (int64_t)j0 * D);
-      const char* vb = reinterpret_cast<const char*>(vp + (int64_t)j0 * D);
+      const char* sb = reinterpret_cast<const char*>(src + (int64_t)j0 * D);
 #pragma unroll
-      for (int u = 0; u < NP; ++u) {
-        global_to_lds16(kb + g_off0 + u * kPassBytes, kd + u * kPassBytes);
-        global_to_lds16(vb + g_off0 + u * kPassBytes, vd + u * kPassBytes);
-      }
+      for (int u = 0; u < NP; ++u) global_to_lds16(sb + g_off0 + u * kPassBytes, d + u * kPassBytes);
     } else {
 #pragma unroll
       for (int u = 0; u < NP; ++u) {
         const int row = st_row0 + u * (kPassBytes / T::kRowBytes);
-        const int64_t src = (int64_t)min(j0 + row, n - 1) * T::kRowBytes + st_slot0 * 16;
-        global_to_lds16(reinterpret_cast<const char*>(kp) + src, kd + u * kPassBytes);
-        global_to_lds16(reinterpret_cast<const char*>(vp) + src, vd + u * kPassBytes);
+        const int64_t off = (int64_t)min(j0 + row, n - 1) * T::kRowBytes + st_slot0 * 16;
+        global_to_lds16(reinterpret_cast<const char*>(src) + off, d + u * kPassBytes);
+      }
+    }
+  };
+  auto load_k = [&](auto stage_c, int j0) { copy_block(kp, kbuf(stage_c), j0); };
+  auto load_v = [&](auto stage_c, int j0) { copy_block(vp, vbuf(stage_c), j0); };
+
+  // ---- the three phases of one key block --------------------------------
+  // S^T = K Q^T for the two 32-key halves of a block in LDS stage S (the two
+  // accumulation chains are interleaved so consecutive MFMAs are independent).
+  auto scores = [&](auto stage_c, f32x16 (&sacc)[2]) {
+    const unsigned char* kb = kbuf(stage_c);
+    sacc[0] = f32x16{};
+    sacc[1] = f32x16{};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll
+      for (int sub = 0; sub < 2; ++sub) {
+        const bf16x8 a = as_bf16x8(*reinterpret_cast<const u32x4*>(
+            kb + sub * 32 * T::kRowBytes + k_off[ks]));
+        sacc[sub] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[ks], sacc[sub], 0, 0, 0);
       }
     }
   };
 
-  // Softmax of one block's scores; MASKED selects the path with masking.
-  auto softmax = [&](auto masked_c, f32x16 (&sacc)[2], int j0, u32x4 (&pb)[4]) {
+  // Masking (only for blocks that cross the diagonal or the length limit),
+  // block extreme of the raw scores (max for a non-negative scale, min for a
+  // negative one) and the lazy rescale of the accumulators.
+  auto prepare = [&](auto masked_c, f32x16 (&sacc)[2], int j0) {
     constexpr bool MASKED = decltype(masked_c)::value;
     if (MASKED) {
 #pragma unroll
@@ -199,8 +215,6 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(PrefillParams
           if (j >= n || j > my_last) sacc[sub][i] = neutral;
         }
     }
-    // Block extreme of the raw scores (max for a non-negative scale, min for
-    // a negative one), joined across the two lane halves.
     float traw = sacc[0][0];
     if (POS) {
 #pragma unroll
@@ -220,6 +234,12 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(PrefillParams
 #pragma unroll
       for (int t = 0; t < DT; ++t) oacc[t] *= alpha;
     }
+  };
+
+  // P = exp2(s*c - m_ref) rounded to bf16 (the B operand of P V); the
+  // running sum is taken from the rounded values (dot2 with (1, 1)).
+  auto probabilities = [&](auto masked_c, const f32x16 (&sacc)[2], u32x4 (&pb)[4]) {
+    constexpr bool MASKED = decltype(masked_c)::value;
     const float negm = -mref;
     float psum = 0.f;
 #pragma unroll
@@ -243,36 +263,10 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(PrefillParams
     lsum += psum;
   };
 
-  // One block of keys from LDS buffer S.
-  auto compute_block = [&](auto stage_c, int j0) {
-    constexpr int S = decltype(stage_c)::value;
-    const unsigned char* kb = kbuf(stage_c);
+  // O^T += V^T P^T from LDS stage S; V^T comes from transpose reads of the
+  // row-major block (k-step outer, output tile inner: DT independent chains).
+  auto accumulate = [&](auto stage_c, const u32x4 (&pb)[4]) {
     const unsigned char* vb = vbuf(stage_c);
-
-    // S^T = K Q^T for the two 32-key halves of the block.
-    // (the two accumulation chains are interleaved so consecutive MFMAs are
-    // independent)
-    f32x16 sacc[2] = {f32x16{}, f32x16{}};
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-#pragma unroll
-      for (int sub = 0; sub < 2; ++sub) {
-        const bf16x8 a = as_bf16x8(*reinterpret_cast<const u32x4*>(
-            kb + sub * 32 * T::kRowBytes + k_off[ks]));
-        sacc[sub] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[ks], sacc[sub], 0, 0, 0);
-      }
-    }
-
-    u32x4 pb[4];
-    const bool need_mask = (j0 + kKeys > n) ||
-                           (CAUSAL && j0 + kKeys - 1 > wave_row0 + n - p.Sq);
-    if (need_mask)
-      softmax(std::true_type{}, sacc, j0, pb);
-    else
-      softmax(std::false_type{}, sacc, j0, pb);
-
-    // O^T += V^T P^T; V^T comes from transpose reads of the row-major block.
-    // (k-step outer, output tile inner: DT independent accumulation chains)
 #pragma unroll
     for (int cc = 0; cc < 4; ++cc) {
 #pragma unroll
@@ -285,23 +279,125 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(PrefillParams
     }
   };
 
-  auto step = [&](auto stage_c, int blk) {
-    constexpr int S = decltype(stage_c)::value;
+  // Scheduling of the region holding the next block's score MFMAs and this
+  // block's exponentials: each MFMA occupies the matrix core for 8 passes,
+  // and a wave issues in order, so the MFMAs are spread out with one
+  // K-operand read and a handful of VALU ops after each instead of being
+  // issued back to back (which would hold the VALU work behind them).
+  auto interleave_scores_with_softmax = [&]() {
+#pragma unroll
+    for (int i = 0; i < 2 * KS; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // DS read
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x400, 2, 0);   // transcendental (exp)
+      __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);   // other VALU
+    }
+  };
+
+  // Does any row of this wave see a key of block blk?  (wave-uniform; once
+  // false it stays false for later blocks)
+  auto active = [&](int blk) {
+    return blk < n_blocks && blk * kKeys <= (CAUSAL ? wave_last_row + n - p.Sq : n - 1);
+  };
+  auto needs_mask = [&](int blk) {
     const int j0 = blk * kKeys;
-    // The other stage was last read in the previous step, before its barrier.
-    if (blk + 1 < n_blocks) load_block(std::integral_constant<int, 1 - S>{}, j0 + kKeys);
-    // Does any row of this wave see a key of this block?  (wave-uniform)
-    if (!CAUSAL || j0 <= wave_last_row + n - p.Sq) compute_block(stage_c, j0);
-    wait_vmem();        // this wave's copies of the next block have landed
+    return (j0 + kKeys > n) || (CAUSAL && j0 + kKeys - 1 > wave_row0 + n - p.Sq);
+  };
+
+  // ---- software-pipelined loop ----------------------------------------
+  // Step blk (LDS parity P = blk % 2) holds K of block blk+1 in K stage 1-P
+  // and V of block blk in V stage P, and has the scores of block blk in
+  // `cur`.  It starts the copies of V(blk+1) into V stage 1-P and of
+  // K(blk+2) into K stage P (both last read in the previous step), then
+  // issues the score MFMAs of block blk+1 -- independent of this block's
+  // softmax, so the matrix cores run them while the vector ALU computes the
+  // exponentials -- and finally P V for block blk.  One barrier per step.
+  auto step = [&](auto par_c, int blk, f32x16 (&cur)[2], f32x16 (&nxt)[2]) {
+    constexpr int P = decltype(par_c)::value;
+    using Pc = std::integral_constant<int, P>;
+    using Qc = std::integral_constant<int, 1 - P>;
+    if (blk + 1 < n_blocks) load_v(Qc{}, (blk + 1) * kKeys);
+    if (blk + 2 < n_blocks) load_k(Pc{}, (blk + 2) * kKeys);
+    const bool act = active(blk), act_next = active(blk + 1);
+    if (act) {
+      u32x4 pb[4];
+      if (!needs_mask(blk)) {
+        prepare(std::false_type{}, cur, blk * kKeys);
+        if (act_next) {
+          scores(Qc{}, nxt);
+          probabilities(std::false_type{}, cur, pb);
+          interleave_scores_with_softmax();
+        } else {
+          probabilities(std::false_type{}, cur, pb);
+        }
+      } else {
+        prepare(std::true_type{}, cur, blk * kKeys);
+        if (act_next) scores(Qc{}, nxt);
+        probabilities(std::true_type{}, cur, pb);
+      }
+      // keep P V in its own scheduling region (hoisting its LDS reads above
+      // the softmax would only raise register pressure)
+      __builtin_amdgcn_sched_barrier(0);
+      accumulate(Pc{}, pb);
+    }
+    wait_vmem();        // this wave's copies have landed
     __syncthreads();    // ... and every other wave's
   };
 
-  if (n_blocks > 0) load_block(std::integral_constant<int, 0>{}, 0);
-  wait_vmem();
-  __syncthreads();
-  for (int blk = 0; blk < n_blocks; blk += 2) {
-    step(std::integral_constant<int, 0>{}, blk);
-    if (blk + 1 < n_blocks) step(std::integral_constant<int, 1>{}, blk + 1);
+  // Non-causal attention uses the plain order (scores, softmax, P V per
+  // block, K and V of block blk+1 fetched during step blk): with every block
+  // active the pipelined form's extra score buffer does not fit the register
+  // budget of two waves per SIMD.
+  auto step_plain = [&](auto par_c, int blk) {
+    constexpr int P = decltype(par_c)::value;
+    using Pc = std::integral_constant<int, P>;
+    using Qc = std::integral_constant<int, 1 - P>;
+    if (blk + 1 < n_blocks) {
+      load_k(Qc{}, (blk + 1) * kKeys);
+      load_v(Qc{}, (blk + 1) * kKeys);
+    }
+    f32x16 sc[2];
+    u32x4 pb[4];
+    scores(Pc{}, sc);
+    if (!needs_mask(blk)) {
+      prepare(std::false_type{}, sc, blk * kKeys);
+      probabilities(std::false_type{}, sc, pb);
+    } else {
+      prepare(std::true_type{}, sc, blk * kKeys);
+      probabilities(std::true_type{}, sc, pb);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    accumulate(Pc{}, pb);
+    wait_vmem();
+    __syncthreads();
+  };
+
+  if constexpr (CAUSAL) {
+    f32x16 sA[2], sB[2];
+    if (n_blocks > 0) {
+      load_k(std::integral_constant<int, 0>{}, 0);
+      load_v(std::integral_constant<int, 0>{}, 0);
+      if (n_blocks > 1) load_k(std::integral_constant<int, 1>{}, kKeys);
+    }
+    wait_vmem();
+    __syncthreads();
+    if (active(0)) scores(std::integral_constant<int, 0>{}, sA);
+    __syncthreads();      // K stage 0 is refilled by step 0
+    for (int blk = 0; blk < n_blocks; blk += 2) {
+      step(std::integral_constant<int, 0>{}, blk, sA, sB);
+      if (blk + 1 < n_blocks) step(std::integral_constant<int, 1>{}, blk + 1, sB, sA);
+    }
+  } else {
+    if (n_blocks > 0) {
+      load_k(std::integral_constant<int, 0>{}, 0);
+      load_v(std::integral_constant<int, 0>{}, 0);
+    }
+    wait_vmem();
+    __syncthreads();
+    for (int blk = 0; blk < n_blocks; blk += 2) {
+      step_plain(std::integral_constant<int, 0>{}, blk);
+      if (blk + 1 < n_blocks) step_plain(std::integral_constant<int, 1>{}, blk + 1);
+    }
   }
 
   // Epilogue: O = O_acc / l, rounded to bf16.

@@ -100,8 +100,17 @@ def test_workspace_bytes(lib):
 
 
 def test_workspace_follows_chunk_override(lib, monkeypatch):
-    base = attn.attn_decode_workspace_bytes(1, 4, 1, 4096, 128)
+    # one query head per KV head: chunked splits
+    base = attn.attn_decode_workspace_bytes(1, 4, 4, 4096, 128)
     monkeypatch.setenv("ATTN_DECODE_CHUNK", "256")
-    forced = attn.attn_decode_workspace_bytes(1, 4, 1, 4096, 128)
+    forced = attn.attn_decode_workspace_bytes(1, 4, 4, 4096, 128)
     # 16 splits of 256 keys: 4 heads x 16 x (128 + 1) floats
     assert forced >= 4 * 16 * 129 * 4 and forced >= base
+
+
+def test_workspace_balanced_query_groups(lib, monkeypatch):
+    # query groups use 128-key units: one partial slot per unit and query head
+    ws = attn.attn_decode_workspace_bytes(2, 8, 2, 1000, 128)
+    assert ws >= 2 * 8 * 8 * 129 * 4
+    monkeypatch.setenv("ATTN_DECODE_CHUNK", "4096")     # no effect on the balanced pass
+    assert attn.attn_decode_workspace_bytes(2, 8, 2, 1000, 128) == ws

@@ -119,8 +119,9 @@ def test_decode_matches_oracle(case):
 @pytest.mark.parametrize("chunk", ["256", "512", "1536"])
 def test_decode_split_count_invariance(chunk, monkeypatch):
     """Any split of the cache merges to the same result (within tolerance),
-    checked against the oracle for each forced chunk size."""
-    B, Hq, Hkv, S, d = 3, 8, 2, 3000, 128
+    checked against the oracle for each forced chunk size (one query head per
+    KV head: the chunked split pass)."""
+    B, Hq, Hkv, S, d = 3, 4, 4, 3000, 128
     lens = [3000, 1537, 255]
     say(f"decode split chunk={chunk}")
     x = make(B, Hq, Hkv, 1, S, d, seed=5, k_mult=4.0)
@@ -129,6 +130,53 @@ def test_decode_split_count_invariance(chunk, monkeypatch):
     torch.cuda.synchronize()
     ref = oracle.decode(x["q"].cpu(), x["k"].cpu(), x["v"].cpu(), lens, 1.0 / np.sqrt(d))
     assert_close(o, ref, torch.bfloat16, f"chunk {chunk}")
+
+
+@pytest.mark.parametrize("wgs", ["1", "3", "7", "64", "100000"])
+def test_decode_balanced_partition_invariance(wgs, monkeypatch):
+    """Query groups: the balanced pass spreads 128-key units over a forced
+    number of workgroups (one workgroup walking every head, a few, more than
+    there are units); every partition merges to the oracle's result.  Lengths
+    include 0 and unit boundaries, and batches with no work sit between
+    others."""
+    B, Hq, Hkv, S, d = 9, 8, 2, 1100, 128
+    lens = [1100, 0, 128, 129, 0, 255, 256, 1, 0]
+    say(f"decode balanced workgroups={wgs}")
+    x = make(B, Hq, Hkv, 1, S, d, seed=15, k_mult=4.0)
+    monkeypatch.setenv("ATTN_DECODE_WORKGROUPS", wgs)
+    o = attn.decode(x["q"], x["k"], x["v"], kv_lens=lens_tensor(lens))
+    torch.cuda.synchronize()
+    ref = oracle.decode(x["q"].cpu(), x["k"].cpu(), x["v"].cpu(), lens, 1.0 / np.sqrt(d))
+    assert_close(o, ref, torch.bfloat16, f"workgroups {wgs}")
+
+
+def test_decode_balanced_many_batches():
+    """A batch larger than a workgroup's scan width per thread (several
+    batches per thread in the prefix sum), ragged lengths with zeros."""
+    B, Hq, Hkv, S, d = 300, 4, 1, 300, 64
+    g = np.random.default_rng(9)
+    lens = [int(x) for x in g.integers(0, S + 1, B)]
+    lens[5] = lens[77] = lens[299] = 0
+    say("decode balanced B=300")
+    x = make(B, Hq, Hkv, 1, S, d, seed=16)
+    o = attn.decode(x["q"], x["k"], x["v"], kv_lens=lens_tensor(lens))
+    torch.cuda.synchronize()
+    ref = oracle.decode(x["q"].cpu(), x["k"].cpu(), x["v"].cpu(), lens, 1.0 / np.sqrt(d))
+    assert_close(o, ref, torch.bfloat16, "B=300")
+
+
+def test_decode_chunked_fallback_for_large_batches():
+    """Past the balanced pass's batch limit query groups use the chunked
+    split pass."""
+    B, Hq, Hkv, S, d = 2100, 2, 1, 40, 64
+    g = np.random.default_rng(10)
+    lens = [int(x) for x in g.integers(0, S + 1, B)]
+    say("decode query groups, B=2100 (chunked pass)")
+    x = make(B, Hq, Hkv, 1, S, d, seed=17)
+    o = attn.decode(x["q"], x["k"], x["v"], kv_lens=lens_tensor(lens))
+    torch.cuda.synchronize()
+    ref = oracle.decode(x["q"].cpu(), x["k"].cpu(), x["v"].cpu(), lens, 1.0 / np.sqrt(d))
+    assert_close(o, ref, torch.bfloat16, "B=2100")
 
 
 # ---------------------------------------------------------------------------
