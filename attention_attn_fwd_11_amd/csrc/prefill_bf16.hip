@@ -8,7 +8,10 @@
 // end.  The score matrix never leaves the chip.
 //
 // gfx950 design
-//   - 256 threads = 4 waves; each wave owns 32 query rows (128 per workgroup).
+//   - 512 threads = 8 waves; each wave owns 32 query rows (256 per workgroup,
+//     one workgroup per CU).  Large tiles halve the K/V traffic per query
+//     row against 128-row tiles; the eight waves (two per SIMD) hide each
+//     other's softmax behind their matrix work.
 //   - Scores are formed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16:
 //     K rows (from LDS) are the A operand and Q^T (held in registers for the
 //     whole loop) is the B operand.  In the accumulator each lane then holds
@@ -19,13 +22,15 @@
 //     consistently on both operands, which leaves the sum unchanged).
 //   - V^T is read from the row-major V block in LDS with the LDS transpose
 //     read (ds_read_b64_tr_b16), so V is never transposed in memory.
-//   - K/V blocks of 64 keys are double-buffered in LDS: the next block's
-//     global loads are issued before the current block's matrix work and
-//     written to the other buffer after it; one barrier per block.  The loop
-//     is unrolled over the two buffers so every LDS address is a lane
+//   - K/V blocks of 64 keys rotate through three LDS stages (96 KiB at
+//     d = 128): the copies of block j+2 are issued before the matrix work
+//     of block j, so two blocks are in flight while one is consumed; one
+//     partial wait (the older block only) and one barrier per block.  The
+//     loop is unrolled over the three stages so every LDS address is a lane
 //     constant plus an immediate offset.
-//   - LDS rows are XOR-swizzled at 16-byte granularity so the row-parallel
-//     operand reads and the transpose reads are free of bank conflicts.
+//   - LDS rows are XOR-swizzled at 16-byte granularity (Tile::sw) so the
+//     row-parallel operand reads and the transpose reads are free of bank
+//     conflicts.
 //   - Softmax in base 2: the scale times log2(e) is folded into the FMA that
 //     forms the exponent; the block max is taken on raw scores (v_max3).
 //   - Lazy rescaling: the reference max of a row only moves when a block's
@@ -46,9 +51,10 @@ namespace attn {
 
 namespace {
 
-constexpr int kRows = 128;   // query rows per workgroup
+constexpr int kRows = 256;   // query rows per workgroup
 constexpr int kKeys = 64;    // keys per LDS block
-constexpr int kThreads = 256;
+constexpr int kThreads = 512;
+constexpr int kXcds = 8;                      // accelerator complex dies of an MI355X
 constexpr float kRescaleSlack = 8.f;   // base-2 headroom before the accumulator is rescaled
 
 template <int D>
@@ -57,27 +63,40 @@ struct Tile {
   static constexpr int kRowBytes = D * 2;
   static constexpr int kBytes = kKeys * kRowBytes;        // one K or V block
   static constexpr int kPiecesPerThread = kKeys * kSlots / kThreads;
+  // Swizzle of row r: its 16-byte slot s is stored at slot s ^ sw(r).  With
+  // gfx950's 64 four-byte LDS banks (a row of 16 slots spans them all once)
+  // two access patterns must hit distinct banks: the K-operand read (16
+  // consecutive rows, one slot each: sw must permute 0..15 over 16 rows) and
+  // the transpose read of V (4 rows aligned to 4, 4 consecutive slots each:
+  // the rows' slot quads must not overlap).  For 8-slot rows (d = 64) two
+  // rows share the 64 banks, so the same holds within even and odd rows.
+  __device__ static __forceinline__ int sw(int r) {
+    if (kSlots == 16) return ((r & 3) << 2) | ((r >> 2) & 3);
+    return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
+  }
   // byte offset of (row, 16-byte slot) inside a swizzled block
   __device__ static __forceinline__ uint32_t off(int row, int slot) {
-    return (uint32_t)(row * kSlots + (slot ^ (lds_swizzle(row) & (kSlots - 1)))) * 16u;
+    return (uint32_t)(row * kSlots + (slot ^ sw(row))) * 16u;
   }
 };
 
 // POS: the scale is >= 0, so the block extreme of the raw scores is their
 // max (a negative scale needs their min).
 template <int D, bool CAUSAL, bool POS>
-__global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(PrefillParams p) {
+__global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillParams p) {
   using T = Tile<D>;
   constexpr int KS = D / 16;       // k-steps of the score MFMA (16 features each)
   constexpr int DT = D / 32;       // 32-feature output tiles
   constexpr int NP = T::kPiecesPerThread;
 
-  // Two stages of K and V blocks, as separate arrays so the compiler can see
-  // that filling one stage does not touch the stage being read.
+  // Three stages of K and V blocks, as separate arrays so the compiler can
+  // see that filling one stage does not touch the stages being read.
   __shared__ __attribute__((aligned(16))) unsigned char k_s0[T::kBytes];
   __shared__ __attribute__((aligned(16))) unsigned char k_s1[T::kBytes];
+  __shared__ __attribute__((aligned(16))) unsigned char k_s2[T::kBytes];
   __shared__ __attribute__((aligned(16))) unsigned char v_s0[T::kBytes];
   __shared__ __attribute__((aligned(16))) unsigned char v_s1[T::kBytes];
+  __shared__ __attribute__((aligned(16))) unsigned char v_s2[T::kBytes];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -85,15 +104,31 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(PrefillParams
   const int half = lane >> 5;      // which 8-feature half of a 16-step this lane feeds
   const int col = lane & 31;       // query column of this lane in the accumulators
 
-  // Block -> (query tile, head, batch).  Causal: heaviest (last) tiles first.
+  // Block -> (query tile, head, batch).  Causal: heaviest (last) tiles
+  // first.  Workgroups are dealt to the 8 XCDs round-robin by id (id % 8);
+  // when the (batch, KV head) pairs divide evenly over the XCDs, the order is
+  // arranged so every query head of one KV head lands on the same XCD, which
+  // then serves that KV head's K/V blocks from its own L2.
   const int n_qt = (p.Sq + kRows - 1) / kRows;
-  const int per_tile = p.Hq * p.B;
+  const int G = p.Hq / p.Hkv;
   const int id = blockIdx.x;
-  int qt = id / per_tile;
+  int qt, h, b;
+  if ((p.B * p.Hkv) % kXcds == 0) {
+    const int xcd = id % kXcds, slot = id / kXcds;
+    const int per_qt = (p.B * p.Hkv / kXcds) * G;       // workgroups per query tile per XCD
+    qt = slot / per_qt;
+    const int r = slot % per_qt;
+    const int kv = (r / G) * kXcds + xcd;               // (batch, KV head) index
+    b = kv / p.Hkv;
+    h = (kv % p.Hkv) * G + r % G;
+  } else {
+    const int per_tile = p.Hq * p.B;
+    qt = id / per_tile;
+    h = (id % per_tile) % p.Hq;
+    b = (id % per_tile) / p.Hq;
+  }
   if (CAUSAL) qt = n_qt - 1 - qt;
-  const int h = (id % per_tile) % p.Hq;
-  const int b = (id % per_tile) / p.Hq;
-  const int g = h / (p.Hq / p.Hkv);
+  const int g = h / G;
 
   int n = p.Skv;
   if (p.kv_lens) n = min(max(p.kv_lens[b], 0), p.Skv);
@@ -123,7 +158,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(PrefillParams
   }
 
   // Staging by direct global -> LDS copies.  Copy u of wave w fills the
-  // 1 KiB LDS chunk c = u*4 + w of a block; lane i lands at byte 16*i of
+  // 1 KiB LDS chunk c = u*8 + w of a block; lane i lands at byte 16*i of
   // it, i.e. at (row, physical slot), and so fetches logical slot
   // physical ^ swizzle(row) of that row.  Rows per pass are a multiple of 16,
   // so the swizzle, and hence the lane's byte offset, only shift by a
@@ -131,7 +166,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(PrefillParams
   constexpr int kPassBytes = kThreads * 16;                 // one copy round of all waves
   const int st_byte0 = wave * 1024 + lane * 16;             // LDS byte of copy 0
   const int st_row0 = st_byte0 / T::kRowBytes;
-  const int st_slot0 = (st_byte0 % T::kRowBytes) / 16 ^ (lds_swizzle(st_row0) & (T::kSlots - 1));
+  const int st_slot0 = (st_byte0 % T::kRowBytes) / 16 ^ T::sw(st_row0);
   const uint32_t g_off0 = (uint32_t)(st_row0 * T::kRowBytes + st_slot0 * 16);
   uint32_t k_off[KS];                       // K operand (row col; row col+32 adds a constant)
 #pragma unroll
@@ -157,10 +192,14 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(PrefillParams
   constexpr float neutral = POS ? kNegInf : kPosInf;   // masked raw score
 
   auto kbuf = [&](auto stage_c) -> unsigned char* {
-    if constexpr (decltype(stage_c)::value == 0) return k_s0; else return k_s1;
+    if constexpr (decltype(stage_c)::value == 0) return k_s0;
+    else if constexpr (decltype(stage_c)::value == 1) return k_s1;
+    else return k_s2;
   };
   auto vbuf = [&](auto stage_c) -> unsigned char* {
-    if constexpr (decltype(stage_c)::value == 0) return v_s0; else return v_s1;
+    if constexpr (decltype(stage_c)::value == 0) return v_s0;
+    else if constexpr (decltype(stage_c)::value == 1) return v_s1;
+    else return v_s2;
   };
 
   // Copy one K (or V) block into LDS stage S.  Rows past n are clamped to
@@ -279,21 +318,6 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(PrefillParams
     }
   };
 
-  // Scheduling of the region holding the next block's score MFMAs and this
-  // block's exponentials: each MFMA occupies the matrix core for 8 passes,
-  // and a wave issues in order, so the MFMAs are spread out with one
-  // K-operand read and a handful of VALU ops after each instead of being
-  // issued back to back (which would hold the VALU work behind them).
-  auto interleave_scores_with_softmax = [&]() {
-#pragma unroll
-    for (int i = 0; i < 2 * KS; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // DS read
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
-      __builtin_amdgcn_sched_group_barrier(0x400, 2, 0);   // transcendental (exp)
-      __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);   // other VALU
-    }
-  };
-
   // Does any row of this wave see a key of block blk?  (wave-uniform; once
   // false it stays false for later blocks)
   auto active = [&](int blk) {
@@ -304,100 +328,59 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(PrefillParams
     return (j0 + kKeys > n) || (CAUSAL && j0 + kKeys - 1 > wave_row0 + n - p.Sq);
   };
 
-  // ---- software-pipelined loop ----------------------------------------
-  // Step blk (LDS parity P = blk % 2) holds K of block blk+1 in K stage 1-P
-  // and V of block blk in V stage P, and has the scores of block blk in
-  // `cur`.  It starts the copies of V(blk+1) into V stage 1-P and of
-  // K(blk+2) into K stage P (both last read in the previous step), then
-  // issues the score MFMAs of block blk+1 -- independent of this block's
-  // softmax, so the matrix cores run them while the vector ALU computes the
-  // exponentials -- and finally P V for block blk.  One barrier per step.
-  auto step = [&](auto par_c, int blk, f32x16 (&cur)[2], f32x16 (&nxt)[2]) {
-    constexpr int P = decltype(par_c)::value;
-    using Pc = std::integral_constant<int, P>;
-    using Qc = std::integral_constant<int, 1 - P>;
-    if (blk + 1 < n_blocks) load_v(Qc{}, (blk + 1) * kKeys);
-    if (blk + 2 < n_blocks) load_k(Pc{}, (blk + 2) * kKeys);
-    const bool act = active(blk), act_next = active(blk + 1);
-    if (act) {
+  // ---- the key loop ------------------------------------------------------
+  // Step blk reads LDS stage blk % 3.  It first issues the copies of block
+  // blk+2 into stage (blk+2) % 3, which was last read in step blk-1 (every
+  // wave has passed that step's closing barrier), then does the block's
+  // scores, softmax and P V.  Before its barrier a wave waits only for its
+  // copies of block blk+1: the copies of a block are issued in order, so at
+  // most the 2*NP copies of block blk+2 may remain outstanding.
+  auto step = [&](auto st_c, int blk) {
+    constexpr int S = decltype(st_c)::value;
+    using Sc = std::integral_constant<int, S>;
+    using Sn = std::integral_constant<int, (S + 2) % 3>;
+    const bool more = blk + 2 < n_blocks;
+    if (more) {
+      load_k(Sn{}, (blk + 2) * kKeys);
+      load_v(Sn{}, (blk + 2) * kKeys);
+    }
+    if (active(blk)) {
+      f32x16 sc[2];
       u32x4 pb[4];
+      scores(Sc{}, sc);
       if (!needs_mask(blk)) {
-        prepare(std::false_type{}, cur, blk * kKeys);
-        if (act_next) {
-          scores(Qc{}, nxt);
-          probabilities(std::false_type{}, cur, pb);
-          interleave_scores_with_softmax();
-        } else {
-          probabilities(std::false_type{}, cur, pb);
-        }
+        prepare(std::false_type{}, sc, blk * kKeys);
+        probabilities(std::false_type{}, sc, pb);
       } else {
-        prepare(std::true_type{}, cur, blk * kKeys);
-        if (act_next) scores(Qc{}, nxt);
-        probabilities(std::true_type{}, cur, pb);
+        prepare(std::true_type{}, sc, blk * kKeys);
+        probabilities(std::true_type{}, sc, pb);
       }
       // keep P V in its own scheduling region (hoisting its LDS reads above
       // the softmax would only raise register pressure)
       __builtin_amdgcn_sched_barrier(0);
-      accumulate(Pc{}, pb);
+      accumulate(Sc{}, pb);
     }
-    wait_vmem();        // this wave's copies have landed
-    __syncthreads();    // ... and every other wave's
-  };
-
-  // Non-causal attention uses the plain order (scores, softmax, P V per
-  // block, K and V of block blk+1 fetched during step blk): with every block
-  // active the pipelined form's extra score buffer does not fit the register
-  // budget of two waves per SIMD.
-  auto step_plain = [&](auto par_c, int blk) {
-    constexpr int P = decltype(par_c)::value;
-    using Pc = std::integral_constant<int, P>;
-    using Qc = std::integral_constant<int, 1 - P>;
-    if (blk + 1 < n_blocks) {
-      load_k(Qc{}, (blk + 1) * kKeys);
-      load_v(Qc{}, (blk + 1) * kKeys);
-    }
-    f32x16 sc[2];
-    u32x4 pb[4];
-    scores(Pc{}, sc);
-    if (!needs_mask(blk)) {
-      prepare(std::false_type{}, sc, blk * kKeys);
-      probabilities(std::false_type{}, sc, pb);
-    } else {
-      prepare(std::true_type{}, sc, blk * kKeys);
-      probabilities(std::true_type{}, sc, pb);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    accumulate(Pc{}, pb);
-    wait_vmem();
+    if (more) wait_vmem_leave<2 * NP>();
+    else wait_vmem();
     __syncthreads();
   };
 
-  if constexpr (CAUSAL) {
-    f32x16 sA[2], sB[2];
-    if (n_blocks > 0) {
-      load_k(std::integral_constant<int, 0>{}, 0);
-      load_v(std::integral_constant<int, 0>{}, 0);
-      if (n_blocks > 1) load_k(std::integral_constant<int, 1>{}, kKeys);
-    }
-    wait_vmem();
-    __syncthreads();
-    if (active(0)) scores(std::integral_constant<int, 0>{}, sA);
-    __syncthreads();      // K stage 0 is refilled by step 0
-    for (int blk = 0; blk < n_blocks; blk += 2) {
-      step(std::integral_constant<int, 0>{}, blk, sA, sB);
-      if (blk + 1 < n_blocks) step(std::integral_constant<int, 1>{}, blk + 1, sB, sA);
-    }
+  if (n_blocks > 0) {
+    load_k(std::integral_constant<int, 0>{}, 0);
+    load_v(std::integral_constant<int, 0>{}, 0);
+  }
+  if (n_blocks > 1) {
+    load_k(std::integral_constant<int, 1>{}, kKeys);
+    load_v(std::integral_constant<int, 1>{}, kKeys);
+    wait_vmem_leave<2 * NP>();     // block 0 has landed
   } else {
-    if (n_blocks > 0) {
-      load_k(std::integral_constant<int, 0>{}, 0);
-      load_v(std::integral_constant<int, 0>{}, 0);
-    }
     wait_vmem();
-    __syncthreads();
-    for (int blk = 0; blk < n_blocks; blk += 2) {
-      step_plain(std::integral_constant<int, 0>{}, blk);
-      if (blk + 1 < n_blocks) step_plain(std::integral_constant<int, 1>{}, blk + 1);
-    }
+  }
+  __syncthreads();
+  for (int blk = 0; blk < n_blocks; blk += 3) {
+    step(std::integral_constant<int, 0>{}, blk);
+    if (blk + 1 < n_blocks) step(std::integral_constant<int, 1>{}, blk + 1);
+    if (blk + 2 < n_blocks) step(std::integral_constant<int, 2>{}, blk + 2);
   }
 
   // Epilogue: O = O_acc / l, rounded to bf16.

@@ -59,6 +59,12 @@ PREFILL_CASES = [
     (3, 4, 2, 150, 260, 64, True, [260, 97, 0], "bf16"),
     (2, 2, 2, 64, 64, 128, False, [64, 1], "bf16"),
     (1, 2, 2, 1, 1, 128, True, None, "bf16"),
+    # several 256-row tiles with a ragged tail; B*Hkv a multiple of 8 takes
+    # the XCD-grouped workgroup order
+    (2, 8, 4, 600, 600, 128, True, None, "bf16"),
+    (1, 16, 8, 530, 530, 64, True, None, "bf16"),
+    (1, 8, 8, 700, 640, 128, False, [640], "bf16"),
+    (2, 8, 2, 520, 777, 128, True, [777, 300], "bf16"),
     (1, 2, 2, 128, 128, 64, True, None, "f32"),
     (2, 4, 2, 200, 260, 128, True, [260, 100], "f32"),
     (1, 3, 1, 70, 90, 64, False, None, "f32"),
