@@ -19,6 +19,7 @@ under "other_workloads".  The CPU oracle is timed on a bounded sample of the
 prefill workload as "cpu_baseline".
 """
 import argparse
+import hashlib
 import json
 import math
 import os
@@ -31,12 +32,43 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2516.6      # 256 CUs x 4096 FLOP/clk x 2.4 GHz, dense
 PEAK_HBM_GBPS = 8000.0
 
+# Sources that decide what a kernel does: a stored HBM-traffic figure is only
+# reported while their hash still matches the one it was measured with.
+CSRC = os.path.join(ROOT, "attention_attn_fwd_11_amd", "csrc")
+KERNEL_SOURCES = {
+    "prefill": ["prefill_bf16.hip", "common.hpp", "kernels.hpp"],
+    "decode": ["decode_bf16.hip", "common.hpp", "kernels.hpp", "attn_api.cpp"],
+}
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def sources_sha256(kind):
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES[kind]:
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload, kind):
+    """HBM bytes per launch from the committed counter summary (FETCH_SIZE +
+    WRITE_SIZE, calibrated against a copy kernel of known size), or None if
+    there is none or the kernel sources changed since it was taken."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)["workloads"][workload]
+    except (OSError, KeyError, ValueError):
+        return None
+    if rec.get("sources_sha256") != sources_sha256(kind):
+        return None
+    return rec["hbm_bytes_per_launch"]
+
 
 def parse():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--no-cpu-baseline", action="store_true",
                     help="skip timing the CPU oracle (e.g. under a profiler)")
     ap.add_argument("--no-others", action="store_true",
@@ -45,6 +77,9 @@ def parse():
                     help="target CPU time for the oracle sample")
     ap.add_argument("--only", default=None,
                     help="time one named workload only and print its line (for profiling)")
+    ap.add_argument("--copy-mib", type=int, default=0,
+                    help="with --only: afterwards run a plain device copy of this many MiB "
+                         "(3 times), the reference for calibrating HBM byte counters")
     return ap.parse_args()
 
 
@@ -121,10 +156,23 @@ def only(args, torch, attn, wl, dev):
     ms, all_ms = tm.mean_ms()
     rate = work / (ms * 1e-3) / (1e12 if unit == "TFLOP/s" else 1e9)
     peak = PEAK_BF16_TFLOPS if unit == "TFLOP/s" else PEAK_HBM_GBPS
-    print(json.dumps({"workload": w.name, "shape": w.describe(), "ms": round(ms, 4),
-                      "min_ms": round(min(all_ms), 4), "max_ms": round(max(all_ms), 4),
-                      "rate": round(rate, 2), "unit": unit, "frac": round(rate / peak, 4),
-                      "steps": args.steps, "warmup": args.warmup}), flush=True)
+    line = {"workload": w.name, "shape": w.describe(), "ms": round(ms, 4),
+            "min_ms": round(min(all_ms), 4), "max_ms": round(max(all_ms), 4),
+            "rate": round(rate, 2), "unit": unit, "frac": round(rate / peak, 4),
+            "algorithmic_per_launch": work, "steps": args.steps, "warmup": args.warmup,
+            "sources_sha256": sources_sha256(w.kind)}
+    if args.copy_mib > 0:
+        # elementwise x * 1 over bf16: reads and writes copy_mib MiB once each
+        n = args.copy_mib * (1 << 20) // 2
+        src = torch.randn(n, device=dev).to(torch.bfloat16)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            torch.mul(src, 1.0, out=dst)
+        torch.cuda.synchronize()
+        assert torch.equal(dst, src)
+        line["copy_bytes_each_way"] = n * 2
+    print(json.dumps(line), flush=True)
 
 
 def main():
@@ -207,11 +255,13 @@ def main():
                              "algorithmic_bytes": by}
 
     roof_p = {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS,
-              "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4), "traffic": None,
-              "kernel": "prefill_bf16_kernel<128, causal>", "avg_launch_ms": round(ms_p, 4),
+              "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+              "traffic": measured_traffic(wp.name, "prefill"), "traffic_unit": "bytes/launch",
+              "kernel": "prefill_bf16_kernel<128, true, true>", "avg_launch_ms": round(ms_p, 4),
               "algorithmic_per_launch": flops_p}
     roof_d = {"bound": "hbm", "achieved": round(gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-              "frac": round(gbps / PEAK_HBM_GBPS, 4), "traffic": None,
+              "frac": round(gbps / PEAK_HBM_GBPS, 4),
+              "traffic": measured_traffic(wd.name, "decode"), "traffic_unit": "bytes/launch",
               "kernel": "decode_split_valu<128> + decode_combine<128>",
               "avg_launch_ms": round(ms_d, 4), "algorithmic_per_launch": bytes_d}
     dominant, second = (roof_p, roof_d) if ms_p >= ms_d else (roof_d, roof_p)
