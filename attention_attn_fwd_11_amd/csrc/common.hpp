@@ -89,14 +89,6 @@ __device__ __forceinline__ void global_to_lds16(const void* g, void* lds_base) {
 // global -> LDS copies).
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
-// Waits until at most N of this wave's vector-memory loads are outstanding
-// (they complete in issue order, so the oldest ones are the ones done).
-template <int N>
-__device__ __forceinline__ void wait_vmem_leave() {
-  static_assert(N >= 0 && N < 64, "vmcnt field range");
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
-}
-
 // Value of lane l^32 (the other half of the wave), via v_permlane32_swap:
 // a VALU op, so no trip through the LDS crossbar.  swap(x, x) yields
 // {x of lanes 0-31 in both halves, x of lanes 32-63 in both halves}.

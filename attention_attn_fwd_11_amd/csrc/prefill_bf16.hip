@@ -22,12 +22,14 @@
 //     consistently on both operands, which leaves the sum unchanged).
 //   - V^T is read from the row-major V block in LDS with the LDS transpose
 //     read (ds_read_b64_tr_b16), so V is never transposed in memory.
-//   - K/V blocks of 64 keys rotate through three LDS stages (96 KiB at
-//     d = 128): the copies of block j+2 are issued before the matrix work
-//     of block j, so two blocks are in flight while one is consumed; one
-//     partial wait (the older block only) and one barrier per block.  The
-//     loop is unrolled over the three stages so every LDS address is a lane
+//   - K and V are staged through LDS 128 keys at a time, double-buffered
+//     (128 KiB at d = 128): the copies of the next stage are issued before
+//     the matrix work on the current one, which is done as two 64-key
+//     compute blocks; one barrier per stage.  The loop is unrolled over the
+//     two buffers and the two halves, so every LDS address is a lane
 //     constant plus an immediate offset.
+//   - In the score MFMAs the K fragments of k-step ks+1 are read while the
+//     MFMAs of k-step ks run.
 //   - LDS rows are XOR-swizzled at 16-byte granularity (Tile::sw) so the
 //     row-parallel operand reads and the transpose reads are free of bank
 //     conflicts.
@@ -52,7 +54,8 @@ namespace attn {
 namespace {
 
 constexpr int kRows = 256;   // query rows per workgroup
-constexpr int kKeys = 64;    // keys per LDS block
+constexpr int kKeys = 64;    // keys per compute block
+constexpr int kStage = 128;  // keys per LDS stage (two compute blocks)
 constexpr int kThreads = 512;
 constexpr int kXcds = 8;                      // accelerator complex dies of an MI355X
 constexpr float kRescaleSlack = 8.f;   // base-2 headroom before the accumulator is rescaled
@@ -61,8 +64,9 @@ template <int D>
 struct Tile {
   static constexpr int kSlots = D / 8;                    // 16-byte slots per row
   static constexpr int kRowBytes = D * 2;
-  static constexpr int kBytes = kKeys * kRowBytes;        // one K or V block
-  static constexpr int kPiecesPerThread = kKeys * kSlots / kThreads;
+  static constexpr int kBytes = kStage * kRowBytes;       // one K or V stage
+  static constexpr int kSubBytes = kKeys * kRowBytes;     // one compute block inside it
+  static constexpr int kPiecesPerThread = kStage * kSlots / kThreads;
   // Swizzle of row r: its 16-byte slot s is stored at slot s ^ sw(r).  With
   // gfx950's 64 four-byte LDS banks (a row of 16 slots spans them all once)
   // two access patterns must hit distinct banks: the K-operand read (16
@@ -93,10 +97,8 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillParams
   // see that filling one stage does not touch the stages being read.
   __shared__ __attribute__((aligned(16))) unsigned char k_s0[T::kBytes];
   __shared__ __attribute__((aligned(16))) unsigned char k_s1[T::kBytes];
-  __shared__ __attribute__((aligned(16))) unsigned char k_s2[T::kBytes];
   __shared__ __attribute__((aligned(16))) unsigned char v_s0[T::kBytes];
   __shared__ __attribute__((aligned(16))) unsigned char v_s1[T::kBytes];
-  __shared__ __attribute__((aligned(16))) unsigned char v_s2[T::kBytes];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -158,7 +160,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillParams
   }
 
   // Staging by direct global -> LDS copies.  Copy u of wave w fills the
-  // 1 KiB LDS chunk c = u*8 + w of a block; lane i lands at byte 16*i of
+  // 1 KiB LDS chunk c = u*8 + w of a stage; lane i lands at byte 16*i of
   // it, i.e. at (row, physical slot), and so fetches logical slot
   // physical ^ swizzle(row) of that row.  Rows per pass are a multiple of 16,
   // so the swizzle, and hence the lane's byte offset, only shift by a
@@ -192,21 +194,17 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillParams
   constexpr float neutral = POS ? kNegInf : kPosInf;   // masked raw score
 
   auto kbuf = [&](auto stage_c) -> unsigned char* {
-    if constexpr (decltype(stage_c)::value == 0) return k_s0;
-    else if constexpr (decltype(stage_c)::value == 1) return k_s1;
-    else return k_s2;
+    if constexpr (decltype(stage_c)::value == 0) return k_s0; else return k_s1;
   };
   auto vbuf = [&](auto stage_c) -> unsigned char* {
-    if constexpr (decltype(stage_c)::value == 0) return v_s0;
-    else if constexpr (decltype(stage_c)::value == 1) return v_s1;
-    else return v_s2;
+    if constexpr (decltype(stage_c)::value == 0) return v_s0; else return v_s1;
   };
 
-  // Copy one K (or V) block into LDS stage S.  Rows past n are clamped to
-  // row n-1 (only on the last block) so no byte beyond a sequence is read.
+  // Copy 128 keys of K (or V) into an LDS stage.  Rows past n are clamped
+  // to row n-1 (only in the last stage) so no byte beyond a sequence is read.
   auto copy_block = [&](const uint16_t* src, unsigned char* dst, int j0) {
     unsigned char* d = dst + wave * 1024;
-    if (j0 + kKeys <= n) {
+    if (j0 + kStage <= n) {
       const char* sb = reinterpret_cast<const char*>(src + (int64_t)j0 * D);
 #pragma unroll
       for (int u = 0; u < NP; ++u) global_to_lds16(sb + g_off0 + u * kPassBytes, d + u * kPassBytes);
@@ -223,20 +221,28 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillParams
   auto load_v = [&](auto stage_c, int j0) { copy_block(vp, vbuf(stage_c), j0); };
 
   // ---- the three phases of one key block --------------------------------
-  // S^T = K Q^T for the two 32-key halves of a block in LDS stage S (the two
-  // accumulation chains are interleaved so consecutive MFMAs are independent).
-  auto scores = [&](auto stage_c, f32x16 (&sacc)[2]) {
-    const unsigned char* kb = kbuf(stage_c);
+  // S^T = K Q^T for the two 32-key halves of compute block `sub` of an LDS
+  // stage (the two accumulation chains are interleaved so consecutive MFMAs
+  // are independent; the next k-step's K fragments are read meanwhile).
+  auto scores = [&](auto stage_c, auto sub_c, f32x16 (&sacc)[2]) {
+    const unsigned char* kb = kbuf(stage_c) + decltype(sub_c)::value * T::kSubBytes;
     sacc[0] = f32x16{};
     sacc[1] = f32x16{};
+    u32x4 a[2][2];   // K fragments: [k-step parity][32-key half]
+    a[0][0] = *reinterpret_cast<const u32x4*>(kb + k_off[0]);
+    a[0][1] = *reinterpret_cast<const u32x4*>(kb + 32 * T::kRowBytes + k_off[0]);
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-#pragma unroll
-      for (int sub = 0; sub < 2; ++sub) {
-        const bf16x8 a = as_bf16x8(*reinterpret_cast<const u32x4*>(
-            kb + sub * 32 * T::kRowBytes + k_off[ks]));
-        sacc[sub] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[ks], sacc[sub], 0, 0, 0);
+      if (ks + 1 < KS) {
+        a[(ks + 1) & 1][0] = *reinterpret_cast<const u32x4*>(kb + k_off[ks + 1]);
+        a[(ks + 1) & 1][1] = *reinterpret_cast<const u32x4*>(kb + 32 * T::kRowBytes + k_off[ks + 1]);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
       }
+#pragma unroll
+      for (int sub = 0; sub < 2; ++sub)
+        sacc[sub] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a[ks & 1][sub]), qreg[ks], sacc[sub], 0, 0, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
     }
   };
 
@@ -304,8 +310,8 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillParams
 
   // O^T += V^T P^T from LDS stage S; V^T comes from transpose reads of the
   // row-major block (k-step outer, output tile inner: DT independent chains).
-  auto accumulate = [&](auto stage_c, const u32x4 (&pb)[4]) {
-    const unsigned char* vb = vbuf(stage_c);
+  auto accumulate = [&](auto stage_c, auto sub_c, const u32x4 (&pb)[4]) {
+    const unsigned char* vb = vbuf(stage_c) + decltype(sub_c)::value * T::kSubBytes;
 #pragma unroll
     for (int cc = 0; cc < 4; ++cc) {
 #pragma unroll
@@ -329,25 +335,15 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillParams
   };
 
   // ---- the key loop ------------------------------------------------------
-  // Step blk reads LDS stage blk % 3.  It first issues the copies of block
-  // blk+2 into stage (blk+2) % 3, which was last read in step blk-1 (every
-  // wave has passed that step's closing barrier), then does the block's
-  // scores, softmax and P V.  Before its barrier a wave waits only for its
-  // copies of block blk+1: the copies of a block are issued in order, so at
-  // most the 2*NP copies of block blk+2 may remain outstanding.
-  auto step = [&](auto st_c, int blk) {
-    constexpr int S = decltype(st_c)::value;
-    using Sc = std::integral_constant<int, S>;
-    using Sn = std::integral_constant<int, (S + 2) % 3>;
-    const bool more = blk + 2 < n_blocks;
-    if (more) {
-      load_k(Sn{}, (blk + 2) * kKeys);
-      load_v(Sn{}, (blk + 2) * kKeys);
-    }
+  // An LDS stage holds 128 keys, processed as two 64-key compute blocks; the
+  // copies of the next stage are issued first, and one barrier closes the
+  // stage.
+  const int n_stages = (n_blocks + 1) / 2;
+  auto block = [&](auto st_c, auto sub_c, int blk) {
     if (active(blk)) {
       f32x16 sc[2];
       u32x4 pb[4];
-      scores(Sc{}, sc);
+      scores(st_c, sub_c, sc);
       if (!needs_mask(blk)) {
         prepare(std::false_type{}, sc, blk * kKeys);
         probabilities(std::false_type{}, sc, pb);
@@ -355,32 +351,31 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillParams
         prepare(std::true_type{}, sc, blk * kKeys);
         probabilities(std::true_type{}, sc, pb);
       }
-      // keep P V in its own scheduling region (hoisting its LDS reads above
-      // the softmax would only raise register pressure)
       __builtin_amdgcn_sched_barrier(0);
-      accumulate(Sc{}, pb);
+      accumulate(st_c, sub_c, pb);
     }
-    if (more) wait_vmem_leave<2 * NP>();
-    else wait_vmem();
+  };
+  auto stage_step = [&](auto st_c, int sb) {
+    using Sn = std::integral_constant<int, 1 - decltype(st_c)::value>;
+    if (sb + 1 < n_stages) {
+      load_k(Sn{}, (sb + 1) * kStage);
+      load_v(Sn{}, (sb + 1) * kStage);
+    }
+    block(st_c, std::integral_constant<int, 0>{}, 2 * sb);
+    if (2 * sb + 1 < n_blocks) block(st_c, std::integral_constant<int, 1>{}, 2 * sb + 1);
+    __builtin_amdgcn_sched_barrier(0);
+    wait_vmem();
     __syncthreads();
   };
-
-  if (n_blocks > 0) {
+  if (n_stages > 0) {
     load_k(std::integral_constant<int, 0>{}, 0);
     load_v(std::integral_constant<int, 0>{}, 0);
   }
-  if (n_blocks > 1) {
-    load_k(std::integral_constant<int, 1>{}, kKeys);
-    load_v(std::integral_constant<int, 1>{}, kKeys);
-    wait_vmem_leave<2 * NP>();     // block 0 has landed
-  } else {
-    wait_vmem();
-  }
+  wait_vmem();
   __syncthreads();
-  for (int blk = 0; blk < n_blocks; blk += 3) {
-    step(std::integral_constant<int, 0>{}, blk);
-    if (blk + 1 < n_blocks) step(std::integral_constant<int, 1>{}, blk + 1);
-    if (blk + 2 < n_blocks) step(std::integral_constant<int, 2>{}, blk + 2);
+  for (int sb = 0; sb < n_stages; sb += 2) {
+    stage_step(std::integral_constant<int, 0>{}, sb);
+    if (sb + 1 < n_stages) stage_step(std::integral_constant<int, 1>{}, sb + 1);
   }
 
   // Epilogue: O = O_acc / l, rounded to bf16.
