@@ -40,8 +40,10 @@ attn_status_t check_common(const void* q, const void* k, const void* v, const vo
   if (has_kv && (!k || !v)) return ATTN_ERR_NULL;
   if ((q && !aligned16(q)) || (o && !aligned16(o)) || (k && !aligned16(k)) || (v && !aligned16(v)))
     return ATTN_ERR_ALIGN;
-  // Offsets are formed in 64-bit arithmetic; each head's rows must fit int32 indexing of rows.
-  if ((int64_t)S_kv * d > INT32_MAX || (int64_t)S_q * d > INT32_MAX) return ATTN_ERR_SHAPE;
+  // Within one head the kernels use 32-bit byte offsets (buffer loads among
+  // them), so each head's rows of q, k, v, o must span at most 2^31 - 1 bytes.
+  const int64_t elem = dtype == ATTN_F32 ? 4 : 2;
+  if ((int64_t)S_kv * d * elem > INT32_MAX || (int64_t)S_q * d * elem > INT32_MAX) return ATTN_ERR_SHAPE;
   if ((int64_t)B * H_q > INT32_MAX / 2) return ATTN_ERR_SHAPE;
   return ATTN_OK;
 }

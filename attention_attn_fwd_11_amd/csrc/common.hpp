@@ -85,6 +85,21 @@ __device__ __forceinline__ void global_to_lds16(const void* g, void* lds_base) {
   __builtin_amdgcn_global_load_lds(g, (lds_void*)lds_base, 16, 0, 0);
 }
 
+// Buffer resource over `bytes` bytes starting at `base`, raw (unformatted)
+// dword access: word 3 = 0x00020000 selects the 32-bit data format with no
+// swizzle and no index stride.  Reads at or past `bytes` return zero.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t raw_buffer(const void* base, int32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
+}
+
+// Buffer -> LDS copy of 16 bytes per lane (buffer_load_dwordx4 ... lds): lane
+// i reads rsrc + voff + soff (voff per lane, soff wave-uniform) and writes
+// lds_base + 16*i; lds_base must be wave-uniform (it goes to M0).
+__device__ __forceinline__ void buffer_to_lds16(__amdgpu_buffer_rsrc_t rsrc, void* lds_base, int32_t voff,
+                                                int32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)lds_base, 16, voff, soff, 0, 0);
+}
+
 // Waits for this wave's outstanding vector-memory loads (including direct
 // global -> LDS copies).
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }

@@ -23,9 +23,12 @@
 //   - V^T is read from the row-major V block in LDS with the LDS transpose
 //     read (ds_read_b64_tr_b16), so V is never transposed in memory.
 //   - K and V are staged through LDS 128 keys at a time, double-buffered
-//     (128 KiB at d = 128): the copies of the next stage are issued before
-//     the matrix work on the current one, which is done as two 64-key
-//     compute blocks; one barrier per stage.  The loop is unrolled over the
+//     (128 KiB at d = 128), by buffer loads that write LDS directly; the
+//     matrix work on a stage is done as two 64-key compute blocks, and the
+//     copies of the next stage are issued between them (issuing them before
+//     the first block measured slower); one barrier per stage.  Each copy's
+//     LDS base and global offset are scalars, so a copy costs no vector ALU
+//     work.  The loop is unrolled over the
 //     two buffers and the two halves, so every LDS address is a lane
 //     constant plus an immediate offset.
 //   - In the score MFMAs the K fragments of k-step ks+1 are read while the
@@ -93,8 +96,8 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillParams
   constexpr int DT = D / 32;       // 32-feature output tiles
   constexpr int NP = T::kPiecesPerThread;
 
-  // Three stages of K and V blocks, as separate arrays so the compiler can
-  // see that filling one stage does not touch the stages being read.
+  // Two stages of K and V, as separate arrays so the compiler can see that
+  // filling one stage does not touch the stage being read.
   __shared__ __attribute__((aligned(16))) unsigned char k_s0[T::kBytes];
   __shared__ __attribute__((aligned(16))) unsigned char k_s1[T::kBytes];
   __shared__ __attribute__((aligned(16))) unsigned char v_s0[T::kBytes];
@@ -202,23 +205,25 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillParams
 
   // Copy 128 keys of K (or V) into an LDS stage.  Rows past n are clamped
   // to row n-1 (only in the last stage) so no byte beyond a sequence is read.
-  auto copy_block = [&](const uint16_t* src, unsigned char* dst, int j0) {
-    unsigned char* d = dst + wave * 1024;
+  const __amdgpu_buffer_rsrc_t k_rsrc = raw_buffer(kp, p.Skv * T::kRowBytes);
+  const __amdgpu_buffer_rsrc_t v_rsrc = raw_buffer(vp, p.Skv * T::kRowBytes);
+  const int wave_chunk = __builtin_amdgcn_readfirstlane(wave * 1024);   // scalar LDS offset
+  auto copy_block = [&](__amdgpu_buffer_rsrc_t rsrc, unsigned char* dst, int j0) {
+    unsigned char* d = dst + wave_chunk;
     if (j0 + kStage <= n) {
-      const char* sb = reinterpret_cast<const char*>(src + (int64_t)j0 * D);
 #pragma unroll
-      for (int u = 0; u < NP; ++u) global_to_lds16(sb + g_off0 + u * kPassBytes, d + u * kPassBytes);
+      for (int u = 0; u < NP; ++u)
+        buffer_to_lds16(rsrc, d + u * kPassBytes, (int)g_off0, j0 * T::kRowBytes + u * kPassBytes);
     } else {
 #pragma unroll
       for (int u = 0; u < NP; ++u) {
         const int row = st_row0 + u * (kPassBytes / T::kRowBytes);
-        const int64_t off = (int64_t)min(j0 + row, n - 1) * T::kRowBytes + st_slot0 * 16;
-        global_to_lds16(reinterpret_cast<const char*>(src) + off, d + u * kPassBytes);
+        buffer_to_lds16(rsrc, d + u * kPassBytes, min(j0 + row, n - 1) * T::kRowBytes + st_slot0 * 16, 0);
       }
     }
   };
-  auto load_k = [&](auto stage_c, int j0) { copy_block(kp, kbuf(stage_c), j0); };
-  auto load_v = [&](auto stage_c, int j0) { copy_block(vp, vbuf(stage_c), j0); };
+  auto load_k = [&](auto stage_c, int j0) { copy_block(k_rsrc, kbuf(stage_c), j0); };
+  auto load_v = [&](auto stage_c, int j0) { copy_block(v_rsrc, vbuf(stage_c), j0); };
 
   // ---- the three phases of one key block --------------------------------
   // S^T = K Q^T for the two 32-key halves of compute block `sub` of an LDS
@@ -336,8 +341,9 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillParams
 
   // ---- the key loop ------------------------------------------------------
   // An LDS stage holds 128 keys, processed as two 64-key compute blocks; the
-  // copies of the next stage are issued first, and one barrier closes the
-  // stage.
+  // copies of the next stage are issued between the two blocks (the other
+  // buffer was last read in the previous stage, closed by its barrier), and
+  // one barrier closes the stage.
   const int n_stages = (n_blocks + 1) / 2;
   auto block = [&](auto st_c, auto sub_c, int blk) {
     if (active(blk)) {
@@ -357,11 +363,12 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillParams
   };
   auto stage_step = [&](auto st_c, int sb) {
     using Sn = std::integral_constant<int, 1 - decltype(st_c)::value>;
+    block(st_c, std::integral_constant<int, 0>{}, 2 * sb);
+    __builtin_amdgcn_sched_barrier(0);
     if (sb + 1 < n_stages) {
       load_k(Sn{}, (sb + 1) * kStage);
       load_v(Sn{}, (sb + 1) * kStage);
     }
-    block(st_c, std::integral_constant<int, 0>{}, 2 * sb);
     if (2 * sb + 1 < n_blocks) block(st_c, std::integral_constant<int, 1>{}, 2 * sb + 1);
     __builtin_amdgcn_sched_barrier(0);
     wait_vmem();

@@ -71,6 +71,8 @@ typedef enum {
  *
  *   q [B,H_q,S_q,d], k/v [B,H_kv,S_kv,d], o [B,H_q,S_q,d]   (device, dtype)
  *   B >= 0, S_q >= 0, S_kv >= 0, H_q >= 1, H_kv >= 1, H_q % H_kv == 0.
+ *   One head's rows (S_q*d or S_kv*d elements) span at most 2^31 - 1 bytes
+ *   (else ATTN_ERR_SHAPE).
  *   d: 64 or 128.
  *   causal: 0 or 1; causal with S_q > S_kv is rejected (ATTN_ERR_SHAPE).
  *   scale: finite; the usual value is 1/sqrt(d).

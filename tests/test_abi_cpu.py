@@ -65,6 +65,9 @@ def decode(q=P, k=P, v=P, o=P, B=1, Hq=2, Hkv=2, Sq=1, Skv=8, d=64, causal=0, sc
     (dict(d=96), 3), (dict(d=256), 3), (dict(dtype=5), 3),
     (dict(q=MIS), 4), (dict(o=MIS), 4), (dict(k=MIS), 4), (dict(v=MIS), 4),
     (dict(scale=math.inf), 7), (dict(scale=math.nan), 7),
+    # one head's rows must span at most 2^31 - 1 bytes
+    (dict(Skv=(1 << 23) + 1, d=128), 2), (dict(Sq=(1 << 23) + 1, Skv=(1 << 23) + 1, causal=0, d=128), 2),
+    (dict(Skv=(1 << 22) + 1, d=128, dtype=attn.ATTN_F32), 2),
 ])
 def test_prefill_rejects(lib, kw, code):
     assert prefill(**kw) == code
@@ -81,7 +84,7 @@ def test_prefill_empty_is_noop(lib):
     (dict(Sq=2), 2), (dict(Sq=0), 2), (dict(Hq=6, Hkv=4), 2), (dict(B=-3), 2),
     (dict(dtype=attn.ATTN_F32), 3), (dict(d=32), 3), (dict(Hq=6, Hkv=2), 3), (dict(Hq=64, Hkv=2), 3),
     (dict(ws=NULL), 5), (dict(wsb=16), 5), (dict(ws=MIS), 4), (dict(k=MIS), 4),
-    (dict(scale=-math.inf), 7),
+    (dict(scale=-math.inf), 7), (dict(Skv=(1 << 23) + 1, d=128), 2),
 ])
 def test_decode_rejects(lib, kw, code):
     assert decode(**kw) == code
