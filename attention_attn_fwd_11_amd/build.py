@@ -1,4 +1,5 @@
-"""Build libattn.so: the gfx950 kernels and the C ABI, compiled with hipcc.
+"""Build libattn.so (the gfx950 kernels and the C ABI) and libattn_probe.so
+(a streaming-read probe the benchmark uses for context), with hipcc.
 
     python -m attention_attn_fwd_11_amd.build
 
@@ -15,9 +16,11 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libattn.so")
+PROBE_LIB = os.path.join(PKG, "libattn_probe.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 SOURCES = ["attn_api.cpp", "prefill_f32.hip", "prefill_bf16.hip", "decode_bf16.hip", "util.hip"]
+PROBE_SOURCES = ["read_probe.hip"]
 
 # Device code for gfx950 only.  Packed-fp32 instruction selection is switched
 # off on purpose: ordinary fp32 code is compiled to scalar-lane VALU ops.
@@ -42,21 +45,27 @@ def _compile(src, extra):
     return out, "\n".join(warn)
 
 
-def build(extra=(), verbose=False):
-    """Compile every source and link libattn.so; returns the library path."""
-    os.makedirs(BUILD, exist_ok=True)
-    with cf.ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
-        results = list(ex.map(lambda s: _compile(s, list(extra)), SOURCES))
-    for obj, warn in results:
-        if warn and verbose:
-            print(warn, file=sys.stderr)
-    tmp = LIB + ".tmp"
-    cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp,
-           *[o for o, _ in results]]
+def _link(objs, lib):
+    tmp = lib + ".tmp"
+    cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(extra=(), verbose=False):
+    """Compile every source, link libattn.so and libattn_probe.so; returns the
+    path of libattn.so."""
+    os.makedirs(BUILD, exist_ok=True)
+    srcs = SOURCES + PROBE_SOURCES
+    with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
+        results = dict(zip(srcs, ex.map(lambda s: _compile(s, list(extra)), srcs)))
+    for obj, warn in results.values():
+        if warn and verbose:
+            print(warn, file=sys.stderr)
+    _link([results[s][0] for s in SOURCES], LIB)
+    _link([results[s][0] for s in PROBE_SOURCES], PROBE_LIB)
     return LIB
 
 

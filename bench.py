@@ -135,6 +135,42 @@ def cpu_baseline(w, x, seconds):
     }
 
 
+def read_probe(torch, dev, gib=4):
+    """Streaming-read ceiling on this device: the plain grid-stride read kernel
+    of libattn_probe.so over `gib` GiB, best over a few launch shapes.  Context
+    for the decode figures; the roofline peak stays the published 8 TB/s."""
+    import ctypes
+    lib = ctypes.CDLL(os.path.join(ROOT, "attention_attn_fwd_11_amd", "libattn_probe.so"))
+    lib.attn_probe_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
+                                           ctypes.c_int32, ctypes.c_void_p]
+    lib.attn_probe_out_words.argtypes = [ctypes.c_int32]
+    lib.attn_probe_out_words.restype = ctypes.c_size_t
+    nbytes = gib << 30
+    buf = torch.ones(nbytes // 4, dtype=torch.int32, device=dev)
+    shapes = [2048, 8192, 16384]
+    out = torch.empty(lib.attn_probe_out_words(max(shapes)), dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream().cuda_stream
+    best = {}
+    for blocks in shapes:
+        ts = []
+        for rep in range(6):
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record()
+            rc = lib.attn_probe_stream_read(buf.data_ptr(), nbytes, out.data_ptr(), blocks, stream)
+            b.record()
+            if rc != 0:
+                raise RuntimeError(f"read probe failed ({rc})")
+            torch.cuda.synchronize()
+            if rep:
+                ts.append(a.elapsed_time(b))
+        best[blocks] = nbytes / (min(ts) * 1e-3) / 1e9
+    del buf, out
+    blocks = max(best, key=best.get)
+    return {"gbps": round(best[blocks], 1), "bytes": nbytes, "workgroups": blocks,
+            "kernel": "grid-stride 16-byte loads, 4 in flight per lane (libattn_probe.so)"}
+
+
 def only(args, torch, attn, wl, dev):
     """Warm up and time one workload (nothing else launched in between)."""
     w = wl.BY_NAME[args.only]
@@ -291,6 +327,11 @@ def main():
         "roofline": dominant,
         "roofline_other": second,
         "other_workloads": other,
+    }
+    probe = read_probe(torch, dev)
+    out["context"] = {
+        "read_probe": probe,
+        "decode_frac_of_read_probe": round(gbps / probe["gbps"], 4),
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wp, inputs[wp.name], args.cpu_seconds)
