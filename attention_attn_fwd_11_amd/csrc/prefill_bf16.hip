@@ -45,8 +45,12 @@
 //     from the rounded values (v_dot2 with (1, 1)), so a constant V comes
 //     back exactly.
 //   - Masking code exists only on the path for blocks that cross the causal
-//     diagonal or the length limit; causal tiles are launched heaviest first
-//     and a wave skips the matrix work of a block wholly above its rows.
+//     diagonal or the length limit, and a wave skips the matrix work of a
+//     block wholly above its rows.
+//   - Causal: a workgroup processes the query tiles n_qt-1-p and p in turn,
+//     so every workgroup has the same work; all pairs of one KV head are
+//     consecutive on one XCD (workgroups go to XCD id % 8) and stream its K/V
+//     through the same L2.
 #include <type_traits>
 
 #include "common.hpp"
@@ -109,30 +113,30 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillParams
   const int half = lane >> 5;      // which 8-feature half of a 16-step this lane feeds
   const int col = lane & 31;       // query column of this lane in the accumulators
 
-  // Block -> (query tile, head, batch).  Causal: heaviest (last) tiles
-  // first.  Workgroups are dealt to the 8 XCDs round-robin by id (id % 8);
-  // when the (batch, KV head) pairs divide evenly over the XCDs, the order is
-  // arranged so every query head of one KV head lands on the same XCD, which
-  // then serves that KV head's K/V blocks from its own L2.
+  // Block -> (tile pair, head, batch).  Workgroups are dealt to the 8 XCDs
+  // round-robin by id (id % 8); when the (batch, KV head) pairs divide
+  // evenly over the XCDs, every workgroup of one KV head lands on the same
+  // XCD, which then serves that KV head's K/V blocks from its own L2.
   const int n_qt = (p.Sq + kRows - 1) / kRows;
   const int G = p.Hq / p.Hkv;
   const int id = blockIdx.x;
-  int qt, h, b;
+  // Causal: workgroup pair index pr covers tiles n_qt-1-pr then pr (one
+  // tile when they coincide); non-causal: one tile, pr.
+  const int n_pr = CAUSAL ? (n_qt + 1) / 2 : n_qt;
+  int pr, h, b;
   if ((p.B * p.Hkv) % kXcds == 0) {
     const int xcd = id % kXcds, slot = id / kXcds;
-    const int per_qt = (p.B * p.Hkv / kXcds) * G;       // workgroups per query tile per XCD
-    qt = slot / per_qt;
-    const int r = slot % per_qt;
-    const int kv = (r / G) * kXcds + xcd;               // (batch, KV head) index
+    const int per_kv = G * n_pr;
+    const int kvl = slot / per_kv, r = slot % per_kv;
+    pr = r % n_pr;
+    const int kv = kvl * kXcds + xcd;
     b = kv / p.Hkv;
-    h = (kv % p.Hkv) * G + r % G;
+    h = (kv % p.Hkv) * G + r / n_pr;
   } else {
-    const int per_tile = p.Hq * p.B;
-    qt = id / per_tile;
-    h = (id % per_tile) % p.Hq;
-    b = (id % per_tile) / p.Hq;
+    pr = id % n_pr;
+    h = (id / n_pr) % p.Hq;
+    b = id / (n_pr * p.Hq);
   }
-  if (CAUSAL) qt = n_qt - 1 - qt;
   const int g = h / G;
 
   int n = p.Skv;
@@ -143,6 +147,9 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillParams
   const uint16_t* vp = static_cast<const uint16_t*>(p.v) + ((int64_t)b * p.Hkv + g) * p.Skv * D;
   uint16_t* op = static_cast<uint16_t*>(p.o) + ((int64_t)b * p.Hq + h) * p.Sq * D;
 
+  const int n_pass = (CAUSAL && n_qt - 1 - pr != pr) ? 2 : 1;
+  for (int pass = 0; pass < n_pass; ++pass) {
+  const int qt = CAUSAL ? (pass == 0 ? n_qt - 1 - pr : pr) : pr;
   const int tile_row0 = qt * kRows;
   const int wave_row0 = tile_row0 + wave * 32;
   const int my_row = wave_row0 + col;
@@ -401,12 +408,15 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillParams
       }
     }
   }
+  }  // tile pass
+
 }
 
 template <int D, bool CAUSAL>
 hipError_t launch(const PrefillParams& p, hipStream_t stream) {
   const int n_qt = (p.Sq + kRows - 1) / kRows;
-  dim3 grid((unsigned)n_qt * p.Hq * p.B);
+  const int n_pr = CAUSAL ? (n_qt + 1) / 2 : n_qt;
+  dim3 grid((unsigned)n_pr * p.Hq * p.B);
   if (p.scale_log2 >= 0.f)
     hipLaunchKernelGGL((prefill_bf16_kernel<D, CAUSAL, true>), grid, dim3(kThreads), 0, stream, p);
   else

@@ -65,6 +65,9 @@ PREFILL_CASES = [
     (1, 16, 8, 530, 530, 64, True, None, "bf16"),
     (1, 8, 8, 700, 640, 128, False, [640], "bf16"),
     (2, 8, 2, 520, 777, 128, True, [777, 300], "bf16"),
+    # causal tile pairs: five tiles (a middle tile alone), four tiles at d = 64
+    (1, 4, 2, 1100, 1100, 128, True, None, "bf16"),
+    (1, 8, 8, 1024, 1024, 64, True, None, "bf16"),
     (1, 2, 2, 128, 128, 64, True, None, "f32"),
     (2, 4, 2, 200, 260, 128, True, [260, 100], "f32"),
     (1, 3, 1, 70, 90, 64, False, None, "f32"),
