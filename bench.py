@@ -171,6 +171,45 @@ def read_probe(torch, dev, gib=4):
             "kernel": "grid-stride 16-byte loads, 4 in flight per lane (libattn_probe.so)"}
 
 
+def decode_graph(torch, attn, wl, dev, steps=200):
+    """Launch overhead of a small decode step (B1 H32 L4096 d128, 64 MiB of
+    cache): host wall time per step over `steps` back-to-back eager calls
+    against `steps` replays of the same call captured in a HIP graph."""
+    B, H, L, d = 1, 32, 4096, 128
+    x = wl.random_problem(B, H, H, 1, L, d, dtype="bf16", device=dev, seed=7)
+    lens = torch.full((B,), L, dtype=torch.int32, device=dev)
+    out = torch.empty_like(x["q"])
+    ws = torch.empty(attn.attn_decode_workspace_bytes(B, H, H, L, d), dtype=torch.uint8, device=dev)
+    f = lambda: attn.decode(x["q"], x["k"], x["v"], kv_lens=lens, out=out, workspace=ws)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for _ in range(3):
+            f()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        f()
+    torch.cuda.synchronize()
+
+    def wall(fn):
+        for _ in range(20):
+            fn()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            fn()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) / steps * 1e6
+
+    eager_us = wall(f)
+    graph_us = wall(g.replay)
+    return {"shape": f"decode bf16 B{B} Hq{H} Hkv{H} Sq1 Skv{L} d{d}", "steps": steps,
+            "eager_us_per_step": round(eager_us, 2), "graph_us_per_step": round(graph_us, 2),
+            "kv_bytes": 2 * B * H * L * d * 2}
+
+
 def only(args, torch, attn, wl, dev):
     """Warm up and time one workload (nothing else launched in between)."""
     w = wl.BY_NAME[args.only]
@@ -328,6 +367,7 @@ def main():
         "roofline_other": second,
         "other_workloads": other,
     }
+    other["decode_graph_small"] = decode_graph(torch, attn, wl, dev)
     probe = read_probe(torch, dev)
     out["context"] = {
         "read_probe": probe,
