@@ -9,7 +9,7 @@
 //
 // gfx950 design
 //   - 512 threads = 8 waves; each wave owns 32 query rows (256 per workgroup,
-//     one workgroup per CU).  Large tiles halve the K/V traffic per query
+//     one workgroup per CU at d = 128).  Large tiles halve the K/V traffic per query
 //     row against 128-row tiles; the eight waves (two per SIMD) hide each
 //     other's softmax behind their matrix work.
 //   - Scores are formed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16:
@@ -92,9 +92,11 @@ struct Tile {
 };
 
 // POS: the scale is >= 0, so the block extreme of the raw scores is their
-// max (a negative scale needs their min).
+// max (a negative scale needs their min).  Causal d = 64 is held to 128
+// registers so two workgroups share a CU (four waves per SIMD; its LDS
+// stages take 64 KiB); the other variants run one workgroup per CU.
 template <int D, bool CAUSAL, bool POS>
-__global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillParams p) {
+__global__ __launch_bounds__(kThreads, (D == 64 && CAUSAL) ? 4 : 1) void prefill_bf16_kernel(PrefillParams p) {
   using T = Tile<D>;
   constexpr int KS = D / 16;       // k-steps of the score MFMA (16 features each)
   constexpr int DT = D / 32;       // 32-feature output tiles

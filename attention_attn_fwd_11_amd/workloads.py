@@ -35,7 +35,7 @@ class Workload:
     dtype: str           # "f32" or "bf16"
     causal: bool
     k_mult: float = 1.0
-    len_range: tuple = None   # (lo, hi) inclusive for ragged decode lengths
+    len_range: tuple = None   # (lo, hi) inclusive for ragged KV lengths
     note: str = field(default="", compare=False)
 
     @property
@@ -69,6 +69,12 @@ WORKLOADS = [
              len_range=(256, 8192), note="GQA decode, ragged lengths"),
     Workload("prefill_gqa_bf16_h64kv8s16384", "prefill", 1, 64, 8, 16384, 16384, 128, "bf16",
              True, k_mult=4.0, note="long causal GQA prefill, K scaled by 4"),
+    Workload("prefill_bf16_b4h32s4096_d64", "prefill", 4, 32, 32, 4096, 4096, 64, "bf16", True,
+             note="causal prefill at head dimension 64"),
+    Workload("prefill_chunked_gqa_bf16_b16h32kv8q512", "prefill", 16, 32, 8, 512, 8192, 128,
+             "bf16", True, len_range=(512, 8192),
+             note="chunked prefill: 512 new tokens per sequence over a ragged KV cache "
+                  "(bottom-right causal)"),
 ]
 BY_NAME = {w.name: w for w in WORKLOADS}
 

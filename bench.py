@@ -216,8 +216,11 @@ def only(args, torch, attn, wl, dev):
     x = wl.generate(w, dev)
     o = torch.empty_like(x["q"])
     if w.kind == "prefill":
-        f = lambda: attn.prefill(x["q"], x["k"], x["v"], causal=w.causal, scale=w.scale, out=o)
-        work, unit = wl.prefill_flops(w), "TFLOP/s"
+        lens = x["kv_lens"] if w.len_range else None
+        f = lambda: attn.prefill(x["q"], x["k"], x["v"], causal=w.causal, scale=w.scale,
+                                 kv_lens=lens, out=o)
+        work = wl.prefill_flops(w, x["kv_lens"].cpu() if w.len_range else None)
+        unit = "TFLOP/s"
     else:
         f = lambda: attn.decode(x["q"], x["k"], x["v"], kv_lens=x["kv_lens"], scale=w.scale, out=o)
         work, unit = wl.decode_kv_bytes(w, x["kv_lens"].cpu()), "GB/s"
@@ -271,8 +274,9 @@ def main():
 
     wp = wl.BY_NAME["prefill_bf16_b4h32s4096"]
     wd = wl.BY_NAME["decode_bf16_b64h32l4096"]
-    others = [] if args.no_others else [wl.BY_NAME["decode_gqa_bf16_b128h32kv8"],
-                                        wl.BY_NAME["prefill_gqa_bf16_h64kv8s16384"]]
+    others = [] if args.no_others else [wl.BY_NAME[n] for n in (
+        "decode_gqa_bf16_b128h32kv8", "prefill_gqa_bf16_h64kv8s16384",
+        "prefill_bf16_b4h32s4096_d64", "prefill_chunked_gqa_bf16_b16h32kv8q512")]
     inputs = {w.name: wl.generate(w, dev) for w in [wp, wd, *others]}
     torch.cuda.synchronize()
 
@@ -280,6 +284,7 @@ def main():
         x = inputs[w.name]
         if w.kind == "prefill":
             return lambda: attn.prefill(x["q"], x["k"], x["v"], causal=w.causal, scale=w.scale,
+                                        kv_lens=x["kv_lens"] if w.len_range else None,
                                         out=x.setdefault("o", torch.empty_like(x["q"])))
         return lambda: attn.decode(x["q"], x["k"], x["v"], kv_lens=x["kv_lens"], scale=w.scale,
                                    out=x.setdefault("o", torch.empty_like(x["q"])))
@@ -317,7 +322,7 @@ def main():
         torch.cuda.synchronize()
         ms, _ = tm.mean_ms()
         if w.kind == "prefill":
-            fl = wl.prefill_flops(w)
+            fl = wl.prefill_flops(w, inputs[w.name]["kv_lens"].cpu() if w.len_range else None)
             rate = fl / (ms * 1e-3) / 1e12
             other[w.name] = {"shape": w.describe(), "ms": round(ms, 4), "TFLOP/s": round(rate, 1),
                              "frac_of_mfma_peak": round(rate / PEAK_BF16_TFLOPS, 4),

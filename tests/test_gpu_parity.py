@@ -321,19 +321,23 @@ def test_side_stream_ordering():
 # ---------------------------------------------------------------------------
 # full-size workloads: sampled rows against the oracle + whole-output checks
 # ---------------------------------------------------------------------------
-@pytest.mark.parametrize("name", ["prefill_bf16_b4h32s4096", "prefill_gqa_bf16_h64kv8s16384"])
+@pytest.mark.parametrize("name", ["prefill_bf16_b4h32s4096", "prefill_gqa_bf16_h64kv8s16384",
+                                  "prefill_bf16_b4h32s4096_d64",
+                                  "prefill_chunked_gqa_bf16_b16h32kv8q512"])
 def test_prefill_workload_sampled(name):
     w = wl.BY_NAME[name]
     say(f"workload {name}: {w.describe()}")
     x = wl.generate(w, DEV)
-    o = attn.prefill(x["q"], x["k"], x["v"], causal=w.causal, scale=w.scale)
+    lens = x["kv_lens"] if w.len_range else None
+    o = attn.prefill(x["q"], x["k"], x["v"], causal=w.causal, scale=w.scale, kv_lens=lens)
     torch.cuda.synchronize()
     ok, finite = convex_bound_ok(o, x["v"], w.Hq)
     assert finite and ok, "output outside the convex hull of V"
     S = w.Sq
     extra = [(0, 0, 0), (w.B - 1, w.Hq - 1, S - 1), (0, w.Hq - 1, 127), (0, 1, 128), (0, 2, S - 129)]
     rows = sample_rows(w.B, w.Hq, S, 250, seed=1, extra=extra)
-    ref = oracle.attention_rows(x["q"].cpu(), x["k"].cpu(), x["v"].cpu(), w.causal, w.scale, rows)
+    ref = oracle.attention_rows(x["q"].cpu(), x["k"].cpu(), x["v"].cpu(), w.causal, w.scale, rows,
+                                kv_lens=None if lens is None else lens.cpu().tolist())
     idx = torch.tensor(rows, dtype=torch.long)
     got = o[idx[:, 0], idx[:, 1], idx[:, 2]]
     assert_close(got, ref, torch.bfloat16, f"{name} sampled rows")
