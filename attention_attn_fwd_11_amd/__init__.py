@@ -18,8 +18,8 @@ import torch
 
 __all__ = [
     "ATTN_F32", "ATTN_BF16", "AttnError", "attn_prefill_fwd", "attn_decode_fwd",
-    "attn_decode_workspace_bytes", "attn_status_str", "attn_last_hip_error", "prefill", "decode",
-    "library_path",
+    "attn_decode_paged_fwd", "attn_decode_workspace_bytes", "attn_status_str",
+    "attn_last_hip_error", "prefill", "decode", "decode_paged", "library_path",
 ]
 
 ATTN_F32 = 0
@@ -54,6 +54,9 @@ def _load():
         lib.attn_decode_fwd.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, f32,
                                         vp, ctypes.c_int, vp, sz, vp]
         lib.attn_decode_fwd.restype = ctypes.c_int
+        lib.attn_decode_paged_fwd.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, f32, vp, i32, i32,
+                                              i32, vp, ctypes.c_int, vp, sz, vp]
+        lib.attn_decode_paged_fwd.restype = ctypes.c_int
         lib.attn_decode_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
         lib.attn_decode_workspace_bytes.restype = sz
         lib.attn_status_str.argtypes = [ctypes.c_int]
@@ -76,6 +79,13 @@ def attn_decode_fwd(q, k_cache, v_cache, o, B, H_q, H_kv, S_q, S_kv, d, causal, 
                     dtype, workspace, workspace_bytes, stream):
     return _load().attn_decode_fwd(q, k_cache, v_cache, o, B, H_q, H_kv, S_q, S_kv, d, causal,
                                    scale, kv_lens, dtype, workspace, workspace_bytes, stream)
+
+
+def attn_decode_paged_fwd(q, k_pages, v_pages, o, B, H_q, H_kv, d, scale, block_table, max_blocks,
+                          page_size, num_pages, kv_lens, dtype, workspace, workspace_bytes, stream):
+    return _load().attn_decode_paged_fwd(q, k_pages, v_pages, o, B, H_q, H_kv, d, scale,
+                                         block_table, max_blocks, page_size, num_pages, kv_lens,
+                                         dtype, workspace, workspace_bytes, stream)
 
 
 def attn_decode_workspace_bytes(B, H_q, H_kv, S_kv, d):
@@ -201,4 +211,41 @@ def decode(q, k_cache, v_cache, kv_lens=None, scale=None, out=None, workspace=No
                          ws.numel() * ws.element_size(), ctypes.c_void_p(stream))
     if st != 0:
         raise AttnError(st, "attn_decode_fwd")
+    return o
+
+
+def decode_paged(q, k_pages, v_pages, block_table, kv_lens=None, scale=None, out=None,
+                 workspace=None):
+    """Single-query decode over a paged cache.  q [B,H_q,1,d] bf16; k_pages,
+    v_pages [num_pages,H_kv,page_size,d] bf16; block_table int32 [B,max_blocks]
+    (page of each sequence's page_size-key block); kv_lens int32 [B] or None.
+
+    Returns o [B,H_q,1,d] bf16, on torch's current stream; the workspace (if
+    not given) is cached per device.
+    """
+    for name, t in (("q", q), ("k_pages", k_pages), ("v_pages", v_pages)):
+        _check_tensor(name, t, torch.bfloat16)
+        if t.dim() != 4:
+            raise ValueError(f"{name} must be 4-dimensional")
+    _check_tensor("block_table", block_table, torch.int32)
+    B, H_q, S_q, d = q.shape
+    num_pages, H_kv, page_size, dk = k_pages.shape
+    if tuple(v_pages.shape) != tuple(k_pages.shape) or dk != d or S_q != 1:
+        raise ValueError("inconsistent q / page shapes")
+    if block_table.dim() != 2 or block_table.shape[0] != B or block_table.device != q.device:
+        raise ValueError("block_table must be int32 [B, max_blocks] on q's device")
+    max_blocks = block_table.shape[1]
+    lens = _lens(kv_lens, B, q.device)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    o = out if out is not None else torch.empty_like(q)
+    need = attn_decode_workspace_bytes(B, H_q, H_kv, max_blocks * page_size, d)
+    ws = workspace if workspace is not None else workspace_for(q.device, need)
+    stream = torch.cuda.current_stream(q.device).cuda_stream
+    st = attn_decode_paged_fwd(_ptr(q), _ptr(k_pages), _ptr(v_pages), _ptr(o), B, H_q, H_kv, d,
+                               float(scale), _ptr(block_table), max_blocks, page_size, num_pages,
+                               _ptr(lens), ATTN_BF16, _ptr(ws), ws.numel() * ws.element_size(),
+                               ctypes.c_void_p(stream))
+    if st != 0:
+        raise AttnError(st, "attn_decode_paged_fwd")
     return o

@@ -99,6 +99,67 @@ int device_cus(int* dev_out) {
 
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
+size_t workspace_bytes(int32_t B, int32_t H_q, int32_t H_kv, int32_t S_kv, int32_t d) {
+  if (B <= 0 || S_kv <= 0 || H_q < 1 || H_kv < 1 || H_q % H_kv != 0 || (d != 64 && d != 128))
+    return 0;
+  const int chunk = decode_chunk(B, H_q, H_kv, S_kv);
+  const int64_t n_split = (S_kv + chunk - 1) / chunk;
+  const size_t rows = (size_t)B * H_q * n_split;
+  return round_up(rows * d * sizeof(float), 256) + round_up(rows * sizeof(float), 256);
+}
+
+// Decode after the entry point's own checks (shared by the contiguous and the
+// paged cache; block_table == nullptr selects the contiguous layout).
+attn_status_t run_decode(const void* q, const void* k, const void* v, void* o, int32_t B, int32_t H_q,
+                         int32_t H_kv, int32_t S_kv, int32_t d, float scale, const int32_t* kv_lens,
+                         attn_dtype_t dtype, void* workspace, size_t ws_bytes, void* stream,
+                         const int32_t* block_table, int32_t max_blocks, int32_t page_size,
+                         int32_t num_pages) {
+  if (dtype != ATTN_BF16) return ATTN_ERR_UNSUPPORTED;
+  const int G = H_q / H_kv;
+  if (G != 1 && G != 2 && G != 4 && G != 8 && G != 16) return ATTN_ERR_UNSUPPORTED;
+  if (B == 0) return ATTN_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (S_kv == 0) {
+    hipError_t e = attn::launch_zero_fill(o, (size_t)B * H_q * d * 2, s);
+    return e == hipSuccess ? ATTN_OK : hip_fail("zero-fill launch", e);
+  }
+  const size_t need = workspace_bytes(B, H_q, H_kv, S_kv, d);
+  if (!workspace || ws_bytes < need) return ATTN_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return ATTN_ERR_ALIGN;
+
+  attn::DecodeParams p{};
+  p.q = q; p.k = k; p.v = v; p.o = o; p.kv_lens = kv_lens;
+  p.B = B; p.Hq = H_q; p.Hkv = H_kv; p.Skv = S_kv; p.d = d;
+  p.block_table = block_table; p.max_blocks = max_blocks; p.page_size = page_size;
+  p.num_pages = num_pages;
+  p.chunk = decode_chunk(B, H_q, H_kv, S_kv);
+  p.n_split = (S_kv + p.chunk - 1) / p.chunk;
+  p.n_wg = 0;
+  if (decode_balanced(B, H_q, H_kv)) {
+    // Persistent grid: three resident workgroups per compute unit, never more
+    // than there are units.  Test-only override: ATTN_DECODE_WORKGROUPS.
+    int dev = 0;
+    const int cus = device_cus(&dev);
+    if (cus <= 0) return hip_fail("hipDeviceGetAttribute(multiprocessor count)", hipGetLastError());
+    int64_t wg = 3 * (int64_t)cus;
+    if (const char* env = std::getenv("ATTN_DECODE_WORKGROUPS")) {
+      const long w = std::strtol(env, nullptr, 10);
+      if (w >= 1 && w <= (1 << 20)) wg = w;
+    }
+    const int64_t max_units = (int64_t)B * H_kv * p.n_split;
+    if (wg > max_units) wg = max_units;
+    p.n_wg = (int)wg;
+  }
+  const size_t rows = (size_t)B * H_q * p.n_split;
+  p.part_o = static_cast<float*>(workspace);
+  p.part_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                        round_up(rows * d * sizeof(float), 256));
+  p.scale_log2 = (float)((double)scale * 1.4426950408889634);
+  hipError_t e = attn::launch_decode_bf16(p, s);
+  return e == hipSuccess ? ATTN_OK : hip_fail("decode launch", e);
+}
+
 }  // namespace
 
 extern "C" {
@@ -120,12 +181,7 @@ const char* attn_status_str(attn_status_t s) {
 const char* attn_last_hip_error(void) { return g_hip_error; }
 
 size_t attn_decode_workspace_bytes(int32_t B, int32_t H_q, int32_t H_kv, int32_t S_kv, int32_t d) {
-  if (B <= 0 || S_kv <= 0 || H_q < 1 || H_kv < 1 || H_q % H_kv != 0 || (d != 64 && d != 128))
-    return 0;
-  const int chunk = decode_chunk(B, H_q, H_kv, S_kv);
-  const int64_t n_split = (S_kv + chunk - 1) / chunk;
-  const size_t rows = (size_t)B * H_q * n_split;
-  return round_up(rows * d * sizeof(float), 256) + round_up(rows * sizeof(float), 256);
+  return workspace_bytes(B, H_q, H_kv, S_kv, d);
 }
 
 attn_status_t attn_prefill_fwd(const void* q, const void* k, const void* v, void* o, int32_t B,
@@ -162,47 +218,30 @@ attn_status_t attn_decode_fwd(const void* q, const void* k_cache, const void* v_
                                   scale, dtype);
   if (st != ATTN_OK) return st;
   if (S_q != 1) return ATTN_ERR_SHAPE;
-  if (dtype != ATTN_BF16) return ATTN_ERR_UNSUPPORTED;
-  const int G = H_q / H_kv;
-  if (G != 1 && G != 2 && G != 4 && G != 8 && G != 16) return ATTN_ERR_UNSUPPORTED;
-  if (B == 0) return ATTN_OK;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  if (S_kv == 0) {
-    hipError_t e = attn::launch_zero_fill(o, (size_t)B * H_q * d * 2, s);
-    return e == hipSuccess ? ATTN_OK : hip_fail("zero-fill launch", e);
-  }
-  const size_t need = attn_decode_workspace_bytes(B, H_q, H_kv, S_kv, d);
-  if (!workspace || workspace_bytes < need) return ATTN_ERR_WORKSPACE;
-  if (!aligned16(workspace)) return ATTN_ERR_ALIGN;
+  return run_decode(q, k_cache, v_cache, o, B, H_q, H_kv, S_kv, d, scale, kv_lens, dtype, workspace,
+                    workspace_bytes, stream, nullptr, 0, 0, 0);
+}
 
-  attn::DecodeParams p{};
-  p.q = q; p.k = k_cache; p.v = v_cache; p.o = o; p.kv_lens = kv_lens;
-  p.B = B; p.Hq = H_q; p.Hkv = H_kv; p.Skv = S_kv; p.d = d;
-  p.chunk = decode_chunk(B, H_q, H_kv, S_kv);
-  p.n_split = (S_kv + p.chunk - 1) / p.chunk;
-  p.n_wg = 0;
-  if (decode_balanced(B, H_q, H_kv)) {
-    // Persistent grid: three resident workgroups per compute unit, never more
-    // than there are units.  Test-only override: ATTN_DECODE_WORKGROUPS.
-    int dev = 0;
-    const int cus = device_cus(&dev);
-    if (cus <= 0) return hip_fail("hipDeviceGetAttribute(multiprocessor count)", hipGetLastError());
-    int64_t wg = 3 * (int64_t)cus;
-    if (const char* env = std::getenv("ATTN_DECODE_WORKGROUPS")) {
-      const long w = std::strtol(env, nullptr, 10);
-      if (w >= 1 && w <= (1 << 20)) wg = w;
-    }
-    const int64_t max_units = (int64_t)B * H_kv * p.n_split;
-    if (wg > max_units) wg = max_units;
-    p.n_wg = (int)wg;
-  }
-  const size_t rows = (size_t)B * H_q * p.n_split;
-  p.part_o = static_cast<float*>(workspace);
-  p.part_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) +
-                                        round_up(rows * d * sizeof(float), 256));
-  p.scale_log2 = (float)((double)scale * 1.4426950408889634);
-  hipError_t e = attn::launch_decode_bf16(p, s);
-  return e == hipSuccess ? ATTN_OK : hip_fail("decode launch", e);
+attn_status_t attn_decode_paged_fwd(const void* q, const void* k_pages, const void* v_pages, void* o,
+                                    int32_t B, int32_t H_q, int32_t H_kv, int32_t d, float scale,
+                                    const int32_t* block_table, int32_t max_blocks,
+                                    int32_t page_size, int32_t num_pages, const int32_t* kv_lens,
+                                    attn_dtype_t dtype, void* workspace, size_t workspace_bytes,
+                                    void* stream) {
+  g_hip_error[0] = '\0';
+  if (page_size < attn::kDecodeUnit || page_size % attn::kDecodeUnit != 0 || max_blocks < 1 ||
+      num_pages < 1)
+    return ATTN_ERR_SHAPE;
+  const int64_t cap = (int64_t)max_blocks * page_size;
+  if (cap > INT32_MAX) return ATTN_ERR_SHAPE;
+  attn_status_t st = check_common(q, k_pages, v_pages, o, B, H_q, H_kv, 1, (int32_t)cap, d, 0,
+                                  scale, dtype);
+  if (st != ATTN_OK) return st;
+  if (B > 0 && !block_table) return ATTN_ERR_NULL;
+  if (reinterpret_cast<uintptr_t>(block_table) & 3u) return ATTN_ERR_ALIGN;
+  return run_decode(q, k_pages, v_pages, o, B, H_q, H_kv, (int32_t)cap, d, scale, kv_lens, dtype,
+                    workspace, workspace_bytes, stream, block_table, max_blocks, page_size,
+                    num_pages);
 }
 
 }  // extern "C"

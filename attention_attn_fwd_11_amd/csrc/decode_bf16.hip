@@ -33,6 +33,24 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
 
+// First element of key row j of head (b, hk) in tensor t (K or V): the
+// contiguous cache [B, Hkv, Skv, d], or the page that holds row j.  Every
+// step of the split kernels covers at most 64 keys starting at a multiple of
+// its size inside a kDecodeUnit-aligned block, and page sizes are multiples
+// of kDecodeUnit, so a step's rows are consecutive rows of one page: the
+// kernels look the page up once per step and address rows from there.
+// Table entries are clamped to the pool, so no entry can address memory
+// outside it.
+template <int D>
+__device__ __forceinline__ const uint16_t* kv_row(const void* t, const DecodeParams& p, int b, int hk,
+                                                  int j) {
+  const uint16_t* base = static_cast<const uint16_t*>(t);
+  if (!p.block_table) return base + (((int64_t)b * p.Hkv + hk) * p.Skv + j) * D;
+  int pg = p.block_table[(int64_t)b * p.max_blocks + j / p.page_size];
+  pg = min(max(pg, 0), p.num_pages - 1);
+  return base + (((int64_t)pg * p.Hkv + hk) * p.page_size + j % p.page_size) * D;
+}
+
 // Cross-wave merge of (m, l, o[D]) held by each wave's lanes, then the
 // partial is written by wave 0.  o_lane(d) gives this lane's share of o[d]
 // for the dims it owns (already summed within the wave).
@@ -72,8 +90,6 @@ __global__ __launch_bounds__(kThreads) void decode_split_valu(DecodeParams p) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int kg = lane / LPK;          // key within an instruction's group
   const int dc = lane % LPK;          // 16-byte feature chunk
-  const uint16_t* kp = static_cast<const uint16_t*>(p.k) + ((int64_t)b * p.Hkv + h) * p.Skv * D;
-  const uint16_t* vp = static_cast<const uint16_t*>(p.v) + ((int64_t)b * p.Hkv + h) * p.Skv * D;
   const u32x4 qv = ld16(static_cast<const uint16_t*>(p.q) + ((int64_t)b * p.Hq + h) * D + 8 * dc);
 
   // Which of the 8 keys of this lane's group its reduced score belongs to.
@@ -85,16 +101,18 @@ __global__ __launch_bounds__(kThreads) void decode_split_valu(DecodeParams p) {
   for (int e = 0; e < 8; ++e) o[e] = 0.f;
 
   for (int base = c0 + wave * KB; base < c1; base += kWaves * KB) {
+    const uint16_t* kp = kv_row<D>(p.k, p, b, h, base);   // rows base .. base+KB-1
+    const uint16_t* vp = kv_row<D>(p.v, p, b, h, base);
     u32x4 kr[8], vr[8];
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
-      const int key = min(base + u * KPI + kg, c1 - 1);
-      kr[u] = ld16(kp + (int64_t)key * D + 8 * dc);
+      const int key = min(base + u * KPI + kg, c1 - 1) - base;
+      kr[u] = ld16(kp + key * D + 8 * dc);
     }
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
-      const int key = min(base + u * KPI + kg, c1 - 1);
-      vr[u] = ld16(vp + (int64_t)key * D + 8 * dc);
+      const int key = min(base + u * KPI + kg, c1 - 1) - base;
+      vr[u] = ld16(vp + key * D + 8 * dc);
     }
     // partial dots over this lane's 8 features
     float part[8];
@@ -237,8 +255,6 @@ __global__ __launch_bounds__(kThreads, 3) void decode_split_mfma(DecodeParams p)
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int qcol = lane & 15;          // query column (valid if < G)
   const int grp = lane >> 4;           // 16-lane group
-  const uint16_t* kp = static_cast<const uint16_t*>(p.k) + ((int64_t)b * p.Hkv + hk) * p.Skv * D;
-  const uint16_t* vp = static_cast<const uint16_t*>(p.v) + ((int64_t)b * p.Hkv + hk) * p.Skv * D;
 
   // Q^T as B operand: lane (qcol, grp) holds Q[h0 + qcol][32*ks + 8*grp .. +7].
   bf16x8 qreg[KS];
@@ -264,11 +280,13 @@ __global__ __launch_bounds__(kThreads, 3) void decode_split_mfma(DecodeParams p)
     // V rows of this step: coalesced pieces, row = piece / SLOTS.
     // A full step reads from a uniform base plus lane-constant offsets; the
     // last, partial step clamps rows to the chunk's last valid key.
+    const uint16_t* kp = kv_row<D>(p.k, p, b, hk, base);   // rows base .. base+31
+    const uint16_t* vp = kv_row<D>(p.v, p, b, hk, base);
     u32x4 kr[2][KS];
     u32x4 vr[VP];
     if (base + 32 <= c1) {
-      const char* kb = reinterpret_cast<const char*>(kp + (int64_t)base * D);
-      const char* vbs = reinterpret_cast<const char*>(vp + (int64_t)base * D);
+      const char* kb = reinterpret_cast<const char*>(kp);
+      const char* vbs = reinterpret_cast<const char*>(vp);
 #pragma unroll
       for (int hlf = 0; hlf < 2; ++hlf)
 #pragma unroll
@@ -278,16 +296,16 @@ __global__ __launch_bounds__(kThreads, 3) void decode_split_mfma(DecodeParams p)
     } else {
 #pragma unroll
       for (int hlf = 0; hlf < 2; ++hlf) {
-        const int key = min(base + 16 * hlf + qcol, c1 - 1);
+        const int key = min(base + 16 * hlf + qcol, c1 - 1) - base;
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) kr[hlf][ks] = ld16(kp + (int64_t)key * D + 32 * ks + 8 * grp);
+        for (int ks = 0; ks < KS; ++ks) kr[hlf][ks] = ld16(kp + key * D + 32 * ks + 8 * grp);
       }
 #pragma unroll
       for (int u = 0; u < VP; ++u) {
         const int piece = u * 64 + lane;
         const int row = piece / SLOTS, slot = piece % SLOTS;
-        const int key = min(base + row, c1 - 1);
-        vr[u] = ld16(vp + (int64_t)key * D + slot * 8);
+        const int key = min(base + row, c1 - 1) - base;
+        vr[u] = ld16(vp + key * D + slot * 8);
       }
     }
     // S^T for keys [base, base+16) and [base+16, base+32)
@@ -499,8 +517,6 @@ __global__ __launch_bounds__(kThreads, 3) void decode_split_balanced(DecodeParam
     if (p.kv_lens) n = min(max(p.kv_lens[b], 0), p.Skv);
     const int seg_start = u;
     const int seg_end = min(uend, pre[b] + (hk + 1) * units_b);
-    const uint16_t* kp = static_cast<const uint16_t*>(p.k) + ((int64_t)b * p.Hkv + hk) * p.Skv * D;
-    const uint16_t* vp = static_cast<const uint16_t*>(p.v) + ((int64_t)b * p.Hkv + hk) * p.Skv * D;
 
     // Q^T as B operand: lane (qcol, grp) holds Q[h0 + qcol][32*ks + 8*grp .. +7].
     bf16x8 qreg[KS];
@@ -523,10 +539,12 @@ __global__ __launch_bounds__(kThreads, 3) void decode_split_balanced(DecodeParam
       if (base >= n) continue;                         // this wave's slice is past the length
       // K into registers (A-operand layout); V straight into this wave's LDS
       // region by direct copies (copy w lands lane i at byte w*1024 + 16*i).
+      const uint16_t* kp = kv_row<D>(p.k, p, b, hk, base);   // rows base .. base+31
+      const uint16_t* vp = kv_row<D>(p.v, p, b, hk, base);
       u32x4 kr[2][KS];
       if (base + 32 <= n) {
-        const char* kb = reinterpret_cast<const char*>(kp + (int64_t)base * D);
-        const char* vbs = reinterpret_cast<const char*>(vp + (int64_t)base * D);
+        const char* kb = reinterpret_cast<const char*>(kp);
+        const char* vbs = reinterpret_cast<const char*>(vp);
 #pragma unroll
         for (int hlf = 0; hlf < 2; ++hlf)
 #pragma unroll
@@ -537,14 +555,14 @@ __global__ __launch_bounds__(kThreads, 3) void decode_split_balanced(DecodeParam
       } else {
 #pragma unroll
         for (int hlf = 0; hlf < 2; ++hlf) {
-          const int key = min(base + 16 * hlf + qcol, n - 1);
+          const int key = min(base + 16 * hlf + qcol, n - 1) - base;
 #pragma unroll
-          for (int ks = 0; ks < KS; ++ks) kr[hlf][ks] = ld16(kp + (int64_t)key * D + 32 * ks + 8 * grp);
+          for (int ks = 0; ks < KS; ++ks) kr[hlf][ks] = ld16(kp + key * D + 32 * ks + 8 * grp);
         }
 #pragma unroll
         for (int w = 0; w < VP; ++w) {
-          const int key = min(base + v_row0 + w * kRowsPerCopy, n - 1);
-          global_to_lds16(reinterpret_cast<const char*>(vp + (int64_t)key * D) + v_slot(w) * 16,
+          const int key = min(base + v_row0 + w * kRowsPerCopy, n - 1) - base;
+          global_to_lds16(reinterpret_cast<const char*>(vp + key * D) + v_slot(w) * 16,
                           vb + w * 1024);
         }
       }

@@ -33,6 +33,12 @@ struct DecodeParams {
   int n_split;             // partial slots per (batch, query head)
   int n_wg;                // G >= 2: workgroups of the balanced split pass
   float scale_log2;
+  // Paged cache (block_table != nullptr): k and v are page pools
+  // [num_pages, Hkv, page_size, d]; row j of batch b lives in page
+  // block_table[b * max_blocks + j / page_size] at row j % page_size.
+  // page_size is a multiple of kDecodeUnit; Skv = max_blocks * page_size.
+  const int32_t* block_table;
+  int max_blocks, page_size, num_pages;
 };
 
 // Largest batch the balanced (G >= 2) decode pass handles: its workgroups

@@ -141,3 +141,40 @@ def decode_kv_bytes(w, kv_lens):
     elt = 4 if w.dtype == "f32" else 2
     total = sum(max(0, min(w.Skv, int(x))) for x in kv_lens)
     return 2 * total * w.Hkv * w.d * elt
+
+
+def paged_cache(k, v, kv_lens, page_size, seed=0, spare_pages=3, fill=float("nan")):
+    """Lay a contiguous cache k, v [B,Hkv,S,d] out as page pools.
+
+    Each sequence b gets ceil(kv_lens[b] / page_size) pages, drawn in a
+    seeded random order from a pool of all needed pages plus `spare_pages`;
+    pool rows that hold no valid key (unused pages, rows past a length) are
+    set to `fill`, and table entries past a sequence's pages to out-of-range
+    values, so a read of either shows up in the output.
+    Returns (k_pages, v_pages, block_table) with pools [num_pages,Hkv,P,d]
+    and block_table int32 [B, ceil(S / P)] on k's device.
+    """
+    B, Hkv, S, d = k.shape
+    P = page_size
+    max_blocks = (S + P - 1) // P
+    lens = [max(0, min(S, int(x))) for x in kv_lens]
+    need = [(n + P - 1) // P for n in lens]
+    num_pages = sum(need) + spare_pages
+    g = torch.Generator(device="cpu").manual_seed(seed)
+    perm = torch.randperm(num_pages, generator=g).tolist()
+    table = torch.full((B, max_blocks), -1, dtype=torch.int32)
+    kp = torch.full((num_pages, Hkv, P, d), fill, dtype=k.dtype, device=k.device)
+    vp = torch.full((num_pages, Hkv, P, d), fill, dtype=v.dtype, device=v.device)
+    nxt = 0
+    for b in range(B):
+        for i in range(max_blocks):
+            if i >= need[b]:
+                table[b, i] = -7 if i % 2 else num_pages + 1000
+                continue
+            page = perm[nxt]
+            nxt += 1
+            table[b, i] = page
+            rows = min(P, lens[b] - i * P)
+            kp[page, :, :rows] = k[b, :, i * P:i * P + rows]
+            vp[page, :, :rows] = v[b, :, i * P:i * P + rows]
+    return kp, vp, table.to(k.device)

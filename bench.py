@@ -171,6 +171,31 @@ def read_probe(torch, dev, gib=4):
             "kernel": "grid-stride 16-byte loads, 4 in flight per lane (libattn_probe.so)"}
 
 
+def paged_decode(torch, attn, wl, x, w, steps, warmup, page_size=128):
+    """The ragged GQA decode with its cache in page_size-key pages (only the
+    pages the lengths need, in shuffled order); same algorithmic bytes as the
+    contiguous call."""
+    lens = x["kv_lens"]
+    kp, vp, table = wl.paged_cache(x["k"], x["v"], lens.cpu().tolist(), page_size, seed=8)
+    out = torch.empty_like(x["q"])
+    f = lambda: attn.decode_paged(x["q"], kp, vp, table, kv_lens=lens, scale=w.scale, out=out)
+    for _ in range(warmup):
+        f()
+    torch.cuda.synchronize()
+    tm = Timer(torch)
+    for _ in range(steps):
+        tm(f)
+    torch.cuda.synchronize()
+    ms, _ = tm.mean_ms()
+    by = wl.decode_kv_bytes(w, lens.cpu())
+    del kp, vp
+    return {"shape": w.describe() + f" paged P{page_size}", "ms": round(ms, 4),
+            "GB/s": round(by / (ms * 1e-3) / 1e9, 1),
+            "frac_of_hbm_peak": round(by / (ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
+            "algorithmic_bytes": by,
+            "pages": sum((int(n) + page_size - 1) // page_size for n in lens.cpu().tolist())}
+
+
 def decode_graph(torch, attn, wl, dev, steps=200):
     """Launch overhead of a small decode step (B1 H32 L4096 d128, 64 MiB of
     cache): host wall time per step over `steps` back-to-back eager calls
@@ -372,6 +397,10 @@ def main():
         "roofline_other": second,
         "other_workloads": other,
     }
+    if not args.no_others:
+        wg = wl.BY_NAME["decode_gqa_bf16_b128h32kv8"]
+        other["decode_paged_gqa_bf16_b128h32kv8_p128"] = paged_decode(
+            torch, attn, wl, inputs[wg.name], wg, args.steps, args.warmup)
     other["decode_graph_small"] = decode_graph(torch, attn, wl, dev)
     probe = read_probe(torch, dev)
     out["context"] = {

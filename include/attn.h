@@ -123,6 +123,45 @@ attn_status_t attn_decode_fwd(const void* q, const void* k_cache, const void* v_
  */
 size_t attn_decode_workspace_bytes(int32_t B, int32_t H_q, int32_t H_kv, int32_t S_kv, int32_t d);
 
+/*
+ * Single-query decode over a paged KV cache.
+ *
+ *   q [B,H_q,1,d], o [B,H_q,1,d]   (device, bf16)
+ *   k_pages, v_pages: page pools [num_pages, H_kv, page_size, d] (device,
+ *   bf16); page p holds page_size consecutive key rows of every KV head.
+ *   block_table: device int32 [B, max_blocks]; key row j of sequence b is row
+ *   j % page_size of page block_table[b * max_blocks + j / page_size].
+ *   kv_lens: device int32[B] or NULL (NULL: every sequence has
+ *   max_blocks * page_size keys); values are clamped to
+ *   [0, max_blocks * page_size].  Only the table entries of pages that hold
+ *   rows below a sequence's length are read; an entry outside
+ *   [0, num_pages) is clamped into it (the result is then unspecified, but no
+ *   memory outside the pools is read).
+ *   page_size: a positive multiple of 128; max_blocks >= 1; num_pages >= 1
+ *   (else ATTN_ERR_SHAPE).  max_blocks * page_size plays the role of S_kv in
+ *   every other rule of attn_decode_fwd: the size limits, G = H_q/H_kv in
+ *   {1, 2, 4, 8, 16}, dtype ATTN_BF16, d 64 or 128, and the workspace, which
+ *   must hold attn_decode_workspace_bytes(B, H_q, H_kv,
+ *   max_blocks * page_size, d) bytes.  block_table must be 4-byte aligned
+ *   (ATTN_ERR_ALIGN) and non-NULL when B > 0 (ATTN_ERR_NULL).
+ *
+ * The same split and combine kernels as attn_decode_fwd; only the address of
+ * a key row changes (one table lookup per step of at most 64 keys, which
+ * never straddles a page).  Results are bitwise identical to attn_decode_fwd
+ * on the same keys laid out contiguously.  This is the decode step of
+ * "Optimizing Decoder Attention for LLMs on GPU" (magmadev.ru) over a paged
+ * KV cache, the PagedAttention layout that "What is kernel fusion and how is
+ * it used in LLM serving?" (aivaro.ru), section 6 (tools and libraries),
+ * lists for vLLM.  The pages give no layout; the pool order above keeps each
+ * head's rows of a page contiguous.
+ */
+attn_status_t attn_decode_paged_fwd(const void* q, const void* k_pages, const void* v_pages, void* o,
+                                    int32_t B, int32_t H_q, int32_t H_kv, int32_t d, float scale,
+                                    const int32_t* block_table, int32_t max_blocks,
+                                    int32_t page_size, int32_t num_pages, const int32_t* kv_lens,
+                                    attn_dtype_t dtype, void* workspace, size_t workspace_bytes,
+                                    void* stream);
+
 /* Static, NUL-terminated description of a status code. */
 const char* attn_status_str(attn_status_t s);
 

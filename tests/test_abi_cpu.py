@@ -33,8 +33,8 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
-    assert {"attn_prefill_fwd", "attn_decode_fwd", "attn_decode_workspace_bytes",
-            "attn_status_str", "attn_last_hip_error"} <= set(names)
+    assert {"attn_prefill_fwd", "attn_decode_fwd", "attn_decode_paged_fwd",
+            "attn_decode_workspace_bytes", "attn_status_str", "attn_last_hip_error"} <= set(names)
     for n in names:
         assert hasattr(lib, n), f"libattn.so does not export {n}"
 
@@ -88,6 +88,31 @@ def test_prefill_empty_is_noop(lib):
 ])
 def test_decode_rejects(lib, kw, code):
     assert decode(**kw) == code
+
+
+def decode_paged(q=P, kp=P, vp=P, o=P, B=2, Hq=4, Hkv=4, d=64, scale=0.125, table=P, max_blocks=4,
+                 page=128, pages=8, lens=NULL, dtype=attn.ATTN_BF16, ws=P, wsb=1 << 30):
+    return attn.attn_decode_paged_fwd(q, kp, vp, o, B, Hq, Hkv, d, scale, table, max_blocks, page,
+                                      pages, lens, dtype, ws, wsb, NULL)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=NULL), 1), (dict(o=NULL), 1), (dict(kp=NULL), 1), (dict(vp=NULL), 1), (dict(table=NULL), 1),
+    (dict(page=64), 2), (dict(page=200), 2), (dict(page=0), 2), (dict(max_blocks=0), 2),
+    (dict(pages=0), 2), (dict(Hq=6, Hkv=4), 2), (dict(B=-1), 2),
+    (dict(max_blocks=1 << 24, page=256), 2),                   # capacity beyond int32
+    (dict(max_blocks=(1 << 16) + 1, page=128, d=128), 2),      # one head's rows beyond 2^31 bytes
+    (dict(dtype=attn.ATTN_F32), 3), (dict(d=96), 3), (dict(Hq=6, Hkv=2), 3),
+    (dict(q=MIS), 4), (dict(kp=MIS), 4), (dict(table=ctypes.c_void_p(0x10002)), 4), (dict(ws=MIS), 4),
+    (dict(ws=NULL), 5), (dict(wsb=16), 5),
+    (dict(scale=math.nan), 7),
+])
+def test_decode_paged_rejects(lib, kw, code):
+    assert decode_paged(**kw) == code
+
+
+def test_decode_paged_empty_batch_is_noop(lib):
+    assert decode_paged(B=0, table=NULL, q=NULL, o=NULL) == 0
 
 
 def test_workspace_bytes(lib):

@@ -1,0 +1,84 @@
+"""Paged-cache decode (attn_decode_paged_fwd) against the contiguous decode on
+the same keys (bitwise: the same kernels, only row addresses differ) and
+against the fp64 oracle.  Pool rows that hold no valid key are NaN and table
+entries past each sequence's pages are out of range, so any stray read
+would show up."""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import attention_attn_fwd_11_amd as attn
+import oracle
+from attention_attn_fwd_11_amd import workloads as wl
+from tests.gpu_util import assert_close
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+CASES = [
+    # B, Hq, Hkv, S, d, page_size, lens
+    (3, 8, 8, 1024, 128, 128, [1024, 700, 1]),             # one query head per KV head
+    (4, 16, 4, 2048, 128, 256, [2048, 1500, 129, 0]),      # query groups, balanced pass
+    (2, 8, 1, 512, 64, 128, [512, 300]),                   # d = 64, groups of 8
+    (5, 4, 4, 1000, 64, 384, [1000, 999, 385, 384, 17]),   # page size 3 x 128, ragged capacity
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: f"B{c[0]}-G{c[1] // c[2]}-S{c[3]}-d{c[4]}-P{c[5]}")
+def test_paged_decode_matches_contiguous_and_oracle(case):
+    B, Hq, Hkv, S, d, P, lens = case
+    print(f"paged decode {case}", flush=True)
+    x = wl.random_problem(B, Hq, Hkv, 1, S, d, dtype="bf16", device=DEV, seed=21)
+    scale = 1.0 / np.sqrt(d)
+    lt = torch.tensor(lens, dtype=torch.int32, device=DEV)
+    kp, vp, table = wl.paged_cache(x["k"], x["v"], lens, P, seed=4)
+    o = attn.decode_paged(x["q"], kp, vp, table, kv_lens=lt, scale=scale)
+    # the contiguous reference call gets a cache of capacity max_blocks * P
+    cap = table.shape[1] * P
+    kc = torch.zeros((B, Hkv, cap, d), dtype=torch.bfloat16, device=DEV)
+    vc = torch.zeros_like(kc)
+    kc[:, :, :S] = x["k"]
+    vc[:, :, :S] = x["v"]
+    oc = attn.decode(x["q"], kc, vc, kv_lens=lt, scale=scale)
+    torch.cuda.synchronize()
+    assert torch.equal(o, oc), "paged and contiguous decode differ"
+    ref = oracle.decode(x["q"].cpu(), x["k"].cpu(), x["v"].cpu(), lens, scale)
+    assert_close(o, ref, torch.bfloat16, f"paged decode {case}")
+
+
+def test_paged_decode_large_batch_chunked_pass():
+    """Query groups past the balanced pass's batch limit use the chunked split
+    kernel; its steps go through the same page lookup."""
+    B, Hq, Hkv, S, d, P = 2100, 2, 1, 256, 64, 128
+    print("paged decode, chunked pass", flush=True)
+    x = wl.random_problem(B, Hq, Hkv, 1, S, d, dtype="bf16", device=DEV, seed=22)
+    g = np.random.default_rng(5)
+    lens = g.integers(0, S + 1, B).tolist()
+    lt = torch.tensor(lens, dtype=torch.int32, device=DEV)
+    kp, vp, table = wl.paged_cache(x["k"], x["v"], lens, P, seed=6)
+    o = attn.decode_paged(x["q"], kp, vp, table, kv_lens=lt)
+    oc = attn.decode(x["q"], x["k"], x["v"], kv_lens=lt)
+    torch.cuda.synchronize()
+    assert torch.equal(o, oc)
+    sel = [0, 1, 777, 2099]
+    ref = oracle.decode(x["q"][sel].cpu(), x["k"][sel].cpu(), x["v"][sel].cpu(), [lens[i] for i in sel],
+                        1.0 / np.sqrt(d))
+    assert_close(o[sel], ref, torch.bfloat16, "paged decode chunked pass")
+
+
+def test_paged_decode_full_size_workload_equals_contiguous():
+    """The ragged GQA decode workload laid out in 128-key pages: bitwise equal
+    to the contiguous decode (whose own parity is checked on sampled
+    batches against the oracle)."""
+    w = wl.BY_NAME["decode_gqa_bf16_b128h32kv8"]
+    print(f"paged full size: {w.describe()}", flush=True)
+    x = wl.generate(w, DEV)
+    lens = x["kv_lens"].cpu().tolist()
+    kp, vp, table = wl.paged_cache(x["k"], x["v"], lens, 128, seed=8)
+    o = attn.decode_paged(x["q"], kp, vp, table, kv_lens=x["kv_lens"], scale=w.scale)
+    oc = attn.decode(x["q"], x["k"], x["v"], kv_lens=x["kv_lens"], scale=w.scale)
+    torch.cuda.synchronize()
+    assert torch.equal(o, oc)
