@@ -18,8 +18,9 @@ import torch
 
 __all__ = [
     "ATTN_F32", "ATTN_BF16", "AttnError", "attn_prefill_fwd", "attn_decode_fwd",
-    "attn_decode_paged_fwd", "attn_decode_workspace_bytes", "attn_status_str",
-    "attn_last_hip_error", "prefill", "decode", "decode_paged", "library_path",
+    "attn_decode_paged_fwd", "attn_prefill_varlen_fwd", "attn_decode_workspace_bytes",
+    "attn_status_str", "attn_last_hip_error", "prefill", "prefill_varlen", "decode",
+    "decode_paged", "library_path",
 ]
 
 ATTN_F32 = 0
@@ -54,6 +55,9 @@ def _load():
         lib.attn_decode_fwd.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, f32,
                                         vp, ctypes.c_int, vp, sz, vp]
         lib.attn_decode_fwd.restype = ctypes.c_int
+        lib.attn_prefill_varlen_fwd.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32,
+                                                i32, i32, i32, f32, ctypes.c_int, vp]
+        lib.attn_prefill_varlen_fwd.restype = ctypes.c_int
         lib.attn_decode_paged_fwd.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, f32, vp, i32, i32,
                                               i32, vp, ctypes.c_int, vp, sz, vp]
         lib.attn_decode_paged_fwd.restype = ctypes.c_int
@@ -73,6 +77,13 @@ def _load():
 def attn_prefill_fwd(q, k, v, o, B, H_q, H_kv, S_q, S_kv, d, causal, scale, kv_lens, dtype, stream):
     return _load().attn_prefill_fwd(q, k, v, o, B, H_q, H_kv, S_q, S_kv, d, causal, scale, kv_lens,
                                     dtype, stream)
+
+
+def attn_prefill_varlen_fwd(q, k, v, o, cu_seqlens_q, cu_seqlens_k, B, H_q, H_kv, max_seqlen_q,
+                            max_seqlen_k, total_q, total_k, d, causal, scale, dtype, stream):
+    return _load().attn_prefill_varlen_fwd(q, k, v, o, cu_seqlens_q, cu_seqlens_k, B, H_q, H_kv,
+                                           max_seqlen_q, max_seqlen_k, total_q, total_k, d, causal,
+                                           scale, dtype, stream)
 
 
 def attn_decode_fwd(q, k_cache, v_cache, o, B, H_q, H_kv, S_q, S_kv, d, causal, scale, kv_lens,
@@ -171,6 +182,43 @@ def prefill(q, k, v, causal=True, scale=None, kv_lens=None, out=None):
                           ctypes.c_void_p(stream))
     if st != 0:
         raise AttnError(st, "attn_prefill_fwd")
+    return o
+
+
+def prefill_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, causal=True,
+                   scale=None, out=None):
+    """Attention over packed sequences.  q [total_q,H_q,d]; k, v [total_k,H_kv,d]
+    (bf16); cu_seqlens_q / cu_seqlens_k int32 [B+1] on the device; the
+    max_seqlen_* bound every sequence's length.  Returns o [total_q,H_q,d].
+    Runs on torch's current stream for q's device."""
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _check_tensor(name, t, torch.bfloat16)
+        if t.dim() != 3:
+            raise ValueError(f"{name} must be [total, H, d]")
+    for name, t in (("cu_seqlens_q", cu_seqlens_q), ("cu_seqlens_k", cu_seqlens_k)):
+        _check_tensor(name, t, torch.int32)
+        if t.dim() != 1 or t.device != q.device:
+            raise ValueError(f"{name} must be int32 [B+1] on q's device")
+    if cu_seqlens_q.shape != cu_seqlens_k.shape:
+        raise ValueError("cu_seqlens_q and cu_seqlens_k must have the same length")
+    total_q, H_q, d = q.shape
+    total_k, H_kv, dk = k.shape
+    if tuple(v.shape) != tuple(k.shape) or dk != d:
+        raise ValueError("inconsistent q/k/v shapes")
+    B = cu_seqlens_q.shape[0] - 1
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    o = out if out is not None else torch.empty_like(q)
+    _check_tensor("out", o, torch.bfloat16)
+    if o.shape != q.shape:
+        raise ValueError("out must have q's shape")
+    stream = torch.cuda.current_stream(q.device).cuda_stream
+    st = attn_prefill_varlen_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(cu_seqlens_q),
+                                 _ptr(cu_seqlens_k), B, H_q, H_kv, int(max_seqlen_q),
+                                 int(max_seqlen_k), total_q, total_k, d, int(bool(causal)),
+                                 float(scale), ATTN_BF16, ctypes.c_void_p(stream))
+    if st != 0:
+        raise AttnError(st, "attn_prefill_varlen_fwd")
     return o
 
 

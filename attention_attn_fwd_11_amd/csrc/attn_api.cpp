@@ -208,6 +208,50 @@ attn_status_t attn_prefill_fwd(const void* q, const void* k, const void* v, void
   return e == hipSuccess ? ATTN_OK : hip_fail("prefill launch", e);
 }
 
+attn_status_t attn_prefill_varlen_fwd(const void* q, const void* k, const void* v, void* o,
+                                      const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                                      int32_t B, int32_t H_q, int32_t H_kv, int32_t max_seqlen_q,
+                                      int32_t max_seqlen_k, int32_t total_q, int32_t total_k,
+                                      int32_t d, int32_t causal, float scale, attn_dtype_t dtype,
+                                      void* stream) {
+  g_hip_error[0] = '\0';
+  if (B < 0 || H_q < 1 || H_kv < 1 || max_seqlen_q < 0 || max_seqlen_k < 0 || total_q < 0 ||
+      total_k < 0)
+    return ATTN_ERR_SHAPE;
+  if (H_q % H_kv != 0) return ATTN_ERR_SHAPE;
+  if (causal != 0 && causal != 1) return ATTN_ERR_SHAPE;
+  if (d != 64 && d != 128) return ATTN_ERR_UNSUPPORTED;
+  if (dtype != ATTN_BF16) return ATTN_ERR_UNSUPPORTED;
+  if (!std::isfinite(scale)) return ATTN_ERR_VALUE;
+  const bool has_q = (int64_t)B * max_seqlen_q > 0 && total_q > 0;
+  const bool has_kv = (int64_t)B * max_seqlen_k > 0 && total_k > 0;
+  if (B > 0 && (!cu_seqlens_q || !cu_seqlens_k)) return ATTN_ERR_NULL;
+  if (has_q && (!q || !o)) return ATTN_ERR_NULL;
+  if (has_q && has_kv && (!k || !v)) return ATTN_ERR_NULL;
+  if ((reinterpret_cast<uintptr_t>(cu_seqlens_q) & 3u) || (reinterpret_cast<uintptr_t>(cu_seqlens_k) & 3u))
+    return ATTN_ERR_ALIGN;
+  if ((q && !aligned16(q)) || (o && !aligned16(o)) || (k && !aligned16(k)) || (v && !aligned16(v)))
+    return ATTN_ERR_ALIGN;
+  // K/V rows of one sequence and head are addressed with 32-bit byte offsets.
+  if ((int64_t)max_seqlen_k * H_kv * d * 2 > INT32_MAX) return ATTN_ERR_SHAPE;
+  if ((int64_t)B * H_q > INT32_MAX / 2) return ATTN_ERR_SHAPE;
+  if (!has_q) return ATTN_OK;  // nothing to compute
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (!has_kv) {
+    // no sequence has a key: every row of O is 0
+    hipError_t e = attn::launch_zero_fill(o, (size_t)total_q * H_q * d * 2, s);
+    return e == hipSuccess ? ATTN_OK : hip_fail("zero-fill launch", e);
+  }
+  attn::PrefillParams p{};
+  p.q = q; p.k = k; p.v = v; p.o = o; p.kv_lens = nullptr;
+  p.B = B; p.Hq = H_q; p.Hkv = H_kv; p.Sq = max_seqlen_q; p.Skv = max_seqlen_k; p.d = d;
+  p.causal = causal;
+  p.scale_log2 = (float)((double)scale * 1.4426950408889634);
+  p.cu_q = cu_seqlens_q; p.cu_k = cu_seqlens_k; p.total_q = total_q; p.total_k = total_k;
+  hipError_t e = attn::launch_prefill_bf16(p, s);
+  return e == hipSuccess ? ATTN_OK : hip_fail("prefill launch", e);
+}
+
 attn_status_t attn_decode_fwd(const void* q, const void* k_cache, const void* v_cache, void* o,
                               int32_t B, int32_t H_q, int32_t H_kv, int32_t S_q, int32_t S_kv,
                               int32_t d, int32_t causal, float scale, const int32_t* kv_lens,

@@ -18,6 +18,12 @@ struct PrefillParams {
   int B, Hq, Hkv, Sq, Skv, d;
   int causal;
   float scale_log2;        // scale * log2(e)
+  // Packed sequences (cu_q != nullptr, bf16 only): q, o are [total_q, Hq, d]
+  // and k, v [total_k, Hkv, d]; sequence b owns rows [cu_q[b], cu_q[b+1]) and
+  // [cu_k[b], cu_k[b+1]).  Sq and Skv are then the largest lengths.
+  const int32_t* cu_q;
+  const int32_t* cu_k;
+  int total_q, total_k;
 };
 
 struct DecodeParams {

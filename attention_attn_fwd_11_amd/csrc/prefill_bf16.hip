@@ -141,34 +141,64 @@ __global__ __launch_bounds__(kThreads, (D == 64 && CAUSAL) ? 4 : 1) void prefill
   }
   const int g = h / G;
 
-  int n = p.Skv;
-  if (p.kv_lens) n = min(max(p.kv_lens[b], 0), p.Skv);
+  // This sequence's geometry.  Padded layout [B, H, S, d]: rows of a head are
+  // d apart, S_q query rows, kv_lens[b] (or S_kv) keys.  Packed layout
+  // [total, H, d]: rows are H*d apart and the sequence's lengths come from
+  // the offsets (clamped to the totals and the stated maxima).
+  int sq, n;
+  int64_t qs, kvs;                  // row strides of q/o and of k/v (elements)
+  const uint16_t *qp, *kp, *vp;
+  uint16_t* op;
+  if (p.cu_q) {
+    const int q0 = min(max(p.cu_q[b], 0), p.total_q);
+    const int q1 = min(max(p.cu_q[b + 1], q0), p.total_q);
+    const int k0 = min(max(p.cu_k[b], 0), p.total_k);
+    const int k1 = min(max(p.cu_k[b + 1], k0), p.total_k);
+    sq = min(q1 - q0, p.Sq);
+    n = min(k1 - k0, p.Skv);
+    qs = (int64_t)p.Hq * D;
+    kvs = (int64_t)p.Hkv * D;
+    qp = static_cast<const uint16_t*>(p.q) + (int64_t)q0 * qs + (int64_t)h * D;
+    op = static_cast<uint16_t*>(p.o) + (int64_t)q0 * qs + (int64_t)h * D;
+    kp = static_cast<const uint16_t*>(p.k) + (int64_t)k0 * kvs + (int64_t)g * D;
+    vp = static_cast<const uint16_t*>(p.v) + (int64_t)k0 * kvs + (int64_t)g * D;
+  } else {
+    sq = p.Sq;
+    n = p.Skv;
+    if (p.kv_lens) n = min(max(p.kv_lens[b], 0), p.Skv);
+    qs = D;
+    kvs = D;
+    qp = static_cast<const uint16_t*>(p.q) + ((int64_t)b * p.Hq + h) * p.Sq * D;
+    op = static_cast<uint16_t*>(p.o) + ((int64_t)b * p.Hq + h) * p.Sq * D;
+    kp = static_cast<const uint16_t*>(p.k) + ((int64_t)b * p.Hkv + g) * p.Skv * D;
+    vp = static_cast<const uint16_t*>(p.v) + ((int64_t)b * p.Hkv + g) * p.Skv * D;
+  }
+  const int kv_row_bytes = (int)kvs * 2;
+  // this sequence's own tiles (fewer than the grid's when it is shorter)
+  const int n_qt_b = (sq + kRows - 1) / kRows;
+  const int n_pr_b = CAUSAL ? (n_qt_b + 1) / 2 : n_qt_b;
+  if (pr >= n_pr_b) return;         // uniform over the workgroup, before any barrier
 
-  const uint16_t* qp = static_cast<const uint16_t*>(p.q) + ((int64_t)b * p.Hq + h) * p.Sq * D;
-  const uint16_t* kp = static_cast<const uint16_t*>(p.k) + ((int64_t)b * p.Hkv + g) * p.Skv * D;
-  const uint16_t* vp = static_cast<const uint16_t*>(p.v) + ((int64_t)b * p.Hkv + g) * p.Skv * D;
-  uint16_t* op = static_cast<uint16_t*>(p.o) + ((int64_t)b * p.Hq + h) * p.Sq * D;
-
-  const int n_pass = (CAUSAL && n_qt - 1 - pr != pr) ? 2 : 1;
+  const int n_pass = (CAUSAL && n_qt_b - 1 - pr != pr) ? 2 : 1;
   for (int pass = 0; pass < n_pass; ++pass) {
-  const int qt = CAUSAL ? (pass == 0 ? n_qt - 1 - pr : pr) : pr;
+  const int qt = CAUSAL ? (pass == 0 ? n_qt_b - 1 - pr : pr) : pr;
   const int tile_row0 = qt * kRows;
   const int wave_row0 = tile_row0 + wave * 32;
   const int my_row = wave_row0 + col;
-  const int last_row = min(tile_row0 + kRows, p.Sq) - 1;
+  const int last_row = min(tile_row0 + kRows, sq) - 1;
   int kend = n;
-  if (CAUSAL) kend = min(n, max(0, last_row + n - p.Sq + 1));
+  if (CAUSAL) kend = min(n, max(0, last_row + n - sq + 1));
   const int n_blocks = (kend + kKeys - 1) / kKeys;
-  const int wave_last_row = min(wave_row0 + 31, p.Sq - 1);
-  const int my_last = CAUSAL ? my_row + n - p.Sq : n - 1;   // last key this row sees
+  const int wave_last_row = min(wave_row0 + 31, sq - 1);
+  const int my_last = CAUSAL ? my_row + n - sq : n - 1;   // last key this row sees
 
   // Q^T as the B operand: lane (col, half) holds Q[my_row][16*ks + 8*half .. +7].
   bf16x8 qreg[KS];
   {
-    const int r = min(my_row, p.Sq - 1);
+    const int r = max(min(my_row, sq - 1), 0);
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
-      qreg[ks] = as_bf16x8(ld16(qp + (int64_t)r * D + 16 * ks + 8 * half));
+      qreg[ks] = as_bf16x8(ld16(qp + (int64_t)r * qs + 16 * ks + 8 * half));
   }
 
   // Staging by direct global -> LDS copies.  Copy u of wave w fills the
@@ -178,10 +208,11 @@ __global__ __launch_bounds__(kThreads, (D == 64 && CAUSAL) ? 4 : 1) void prefill
   // so the swizzle, and hence the lane's byte offset, only shift by a
   // constant from one copy to the next.
   constexpr int kPassBytes = kThreads * 16;                 // one copy round of all waves
+  constexpr int kPassRows = kPassBytes / T::kRowBytes;      // key rows it covers
   const int st_byte0 = wave * 1024 + lane * 16;             // LDS byte of copy 0
   const int st_row0 = st_byte0 / T::kRowBytes;
   const int st_slot0 = (st_byte0 % T::kRowBytes) / 16 ^ T::sw(st_row0);
-  const uint32_t g_off0 = (uint32_t)(st_row0 * T::kRowBytes + st_slot0 * 16);
+  const uint32_t g_off0 = (uint32_t)(st_row0 * kv_row_bytes + st_slot0 * 16);
   uint32_t k_off[KS];                       // K operand (row col; row col+32 adds a constant)
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) k_off[ks] = T::off(col, 2 * ks + half);
@@ -214,20 +245,22 @@ __global__ __launch_bounds__(kThreads, (D == 64 && CAUSAL) ? 4 : 1) void prefill
 
   // Copy 128 keys of K (or V) into an LDS stage.  Rows past n are clamped
   // to row n-1 (only in the last stage) so no byte beyond a sequence is read.
-  const __amdgpu_buffer_rsrc_t k_rsrc = raw_buffer(kp, p.Skv * T::kRowBytes);
-  const __amdgpu_buffer_rsrc_t v_rsrc = raw_buffer(vp, p.Skv * T::kRowBytes);
+  // one head's rows of this sequence: (n - 1) strides plus one row
+  const int kv_bytes = n > 0 ? (n - 1) * kv_row_bytes + T::kRowBytes : 0;
+  const __amdgpu_buffer_rsrc_t k_rsrc = raw_buffer(kp, kv_bytes);
+  const __amdgpu_buffer_rsrc_t v_rsrc = raw_buffer(vp, kv_bytes);
   const int wave_chunk = __builtin_amdgcn_readfirstlane(wave * 1024);   // scalar LDS offset
   auto copy_block = [&](__amdgpu_buffer_rsrc_t rsrc, unsigned char* dst, int j0) {
     unsigned char* d = dst + wave_chunk;
     if (j0 + kStage <= n) {
 #pragma unroll
       for (int u = 0; u < NP; ++u)
-        buffer_to_lds16(rsrc, d + u * kPassBytes, (int)g_off0, j0 * T::kRowBytes + u * kPassBytes);
+        buffer_to_lds16(rsrc, d + u * kPassBytes, (int)g_off0, (j0 + u * kPassRows) * kv_row_bytes);
     } else {
 #pragma unroll
       for (int u = 0; u < NP; ++u) {
-        const int row = st_row0 + u * (kPassBytes / T::kRowBytes);
-        buffer_to_lds16(rsrc, d + u * kPassBytes, min(j0 + row, n - 1) * T::kRowBytes + st_slot0 * 16, 0);
+        const int row = st_row0 + u * kPassRows;
+        buffer_to_lds16(rsrc, d + u * kPassBytes, min(j0 + row, n - 1) * kv_row_bytes + st_slot0 * 16, 0);
       }
     }
   };
@@ -341,11 +374,11 @@ __global__ __launch_bounds__(kThreads, (D == 64 && CAUSAL) ? 4 : 1) void prefill
   // Does any row of this wave see a key of block blk?  (wave-uniform; once
   // false it stays false for later blocks)
   auto active = [&](int blk) {
-    return blk < n_blocks && blk * kKeys <= (CAUSAL ? wave_last_row + n - p.Sq : n - 1);
+    return blk < n_blocks && blk * kKeys <= (CAUSAL ? wave_last_row + n - sq : n - 1);
   };
   auto needs_mask = [&](int blk) {
     const int j0 = blk * kKeys;
-    return (j0 + kKeys > n) || (CAUSAL && j0 + kKeys - 1 > wave_row0 + n - p.Sq);
+    return (j0 + kKeys > n) || (CAUSAL && j0 + kKeys - 1 > wave_row0 + n - sq);
   };
 
   // ---- the key loop ------------------------------------------------------
@@ -397,8 +430,8 @@ __global__ __launch_bounds__(kThreads, (D == 64 && CAUSAL) ? 4 : 1) void prefill
   // Epilogue: O = O_acc / l, rounded to bf16.
   const float l = sum_across_halves(lsum);
   const float inv = l > 0.f ? 1.f / l : 0.f;
-  if (my_row < p.Sq) {
-    uint16_t* orow = op + (int64_t)my_row * D;
+  if (my_row < sq) {
+    uint16_t* orow = op + (int64_t)my_row * qs;
 #pragma unroll
     for (int t = 0; t < DT; ++t) {
 #pragma unroll

@@ -178,3 +178,42 @@ def paged_cache(k, v, kv_lens, page_size, seed=0, spare_pages=3, fill=float("nan
             kp[page, :, :rows] = k[b, :, i * P:i * P + rows]
             vp[page, :, :rows] = v[b, :, i * P:i * P + rows]
     return kp, vp, table.to(k.device)
+
+
+def varlen_problem(q_lens, k_lens, Hq, Hkv, d, device="cpu", seed=0):
+    """Packed sequences by the same recipe (Q, then K, then V as float32
+    normals on a generator of `device` seeded with `seed`, cast to bf16):
+    q [sum(q_lens), Hq, d], k and v [sum(k_lens), Hkv, d], and the int32
+    offsets cu_q, cu_k [B+1] on `device`."""
+    dev = torch.device(device)
+    g = torch.Generator(device=dev).manual_seed(seed)
+    tq, tk = int(sum(q_lens)), int(sum(k_lens))
+    q = torch.randn((tq, Hq, d), generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
+    k = torch.randn((tk, Hkv, d), generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
+    v = torch.randn((tk, Hkv, d), generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
+    cu_q = torch.tensor([0] + list(torch.tensor(q_lens).cumsum(0).tolist()), dtype=torch.int32,
+                        device=dev)
+    cu_k = torch.tensor([0] + list(torch.tensor(k_lens).cumsum(0).tolist()), dtype=torch.int32,
+                        device=dev)
+    return {"q": q, "k": k, "v": v, "cu_q": cu_q, "cu_k": cu_k}
+
+
+# Packed variable-length prefill: B sequences, each with as many queries as
+# keys, lengths drawn like the ragged decode lengths (seed 0).
+VARLEN = Workload("prefill_varlen_gqa_bf16_b16h32kv8", "prefill", 16, 32, 8, 4096, 4096, 128, "bf16",
+                  True, len_range=(256, 4096),
+                  note="packed causal prefill, lengths U[256, 4096], q and k lengths equal")
+
+
+def varlen_flops(Hq, d, q_lens, k_lens, causal=True):
+    """Algorithmic FLOPs of a packed call: 4*d per visible pair, per sequence
+    bottom-right causal."""
+    pairs = 0
+    for s, n in zip(q_lens, k_lens):
+        s, n = int(s), int(n)
+        if causal:
+            i = torch.arange(s, dtype=torch.int64)
+            pairs += int((i + (n - s + 1)).clamp(0, n).sum())
+        else:
+            pairs += s * n
+    return 4 * d * Hq * pairs

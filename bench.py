@@ -171,6 +171,30 @@ def read_probe(torch, dev, gib=4):
             "kernel": "grid-stride 16-byte loads, 4 in flight per lane (libattn_probe.so)"}
 
 
+def varlen_prefill(torch, attn, wl, dev, steps, warmup):
+    """Packed causal prefill over sequences of mixed lengths (the varlen
+    workload: q and k lengths equal, drawn from U[256, 4096])."""
+    w = wl.VARLEN
+    lens = wl.kv_lengths(w).tolist()
+    x = wl.varlen_problem(lens, lens, w.Hq, w.Hkv, w.d, device=dev, seed=0)
+    out = torch.empty_like(x["q"])
+    f = lambda: attn.prefill_varlen(x["q"], x["k"], x["v"], x["cu_q"], x["cu_k"], max(lens),
+                                    max(lens), causal=True, scale=w.scale, out=out)
+    for _ in range(warmup):
+        f()
+    torch.cuda.synchronize()
+    tm = Timer(torch)
+    for _ in range(steps):
+        tm(f)
+    torch.cuda.synchronize()
+    ms, _ = tm.mean_ms()
+    fl = wl.varlen_flops(w.Hq, w.d, lens, lens)
+    return {"shape": w.describe() + " packed", "ms": round(ms, 4),
+            "TFLOP/s": round(fl / (ms * 1e-3) / 1e12, 1),
+            "frac_of_mfma_peak": round(fl / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+            "algorithmic_flop": fl, "tokens": sum(lens)}
+
+
 def paged_decode(torch, attn, wl, x, w, steps, warmup, page_size=128):
     """The ragged GQA decode with its cache in page_size-key pages (only the
     pages the lengths need, in shuffled order); same algorithmic bytes as the
@@ -401,6 +425,7 @@ def main():
         wg = wl.BY_NAME["decode_gqa_bf16_b128h32kv8"]
         other["decode_paged_gqa_bf16_b128h32kv8_p128"] = paged_decode(
             torch, attn, wl, inputs[wg.name], wg, args.steps, args.warmup)
+        other[wl.VARLEN.name] = varlen_prefill(torch, attn, wl, dev, args.steps, args.warmup)
     other["decode_graph_small"] = decode_graph(torch, attn, wl, dev)
     probe = read_probe(torch, dev)
     out["context"] = {

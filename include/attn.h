@@ -91,6 +91,35 @@ attn_status_t attn_prefill_fwd(const void* q, const void* k, const void* v, void
                                attn_dtype_t dtype, void* stream);
 
 /*
+ * Attention forward over packed variable-length sequences (bf16).
+ *
+ *   q [total_q, H_q, d], o [total_q, H_q, d]; k, v [total_k, H_kv, d]
+ *   (device, bf16, row-major: the H heads of a token are adjacent).
+ *   cu_seqlens_q, cu_seqlens_k: device int32 [B+1], non-decreasing, starting
+ *   at 0: sequence b owns query rows [cu_seqlens_q[b], cu_seqlens_q[b+1]) and
+ *   key rows [cu_seqlens_k[b], cu_seqlens_k[b+1]).  Their values are read on
+ *   the device: offsets are clamped to [0, total], and a sequence's lengths
+ *   to max_seqlen_q / max_seqlen_k, which must bound them.
+ *   causal: bottom-right per sequence (query i of a sequence with s queries
+ *   and n keys sees key j iff j <= i + n - s); a row that sees no key, also
+ *   every row of a sequence with n = 0, gets O = 0.
+ *   d: 64 or 128; dtype: ATTN_BF16 only (else ATTN_ERR_UNSUPPORTED).
+ *   max_seqlen_k * H_kv * d * 2 <= 2^31 - 1 (else ATTN_ERR_SHAPE).
+ *   cu_seqlens_* must be 4-byte aligned, the tensors 16-byte aligned.
+ *
+ * Per sequence this is the operation of attn_prefill_fwd (the standard
+ * attention of "GPU learning day 24: Operator Fusion", section 3.4), with the
+ * same GQA head map; it runs the same kernel, with the row stride H*d and
+ * each sequence's offsets in place of the padded [B, H, S, d] layout.
+ */
+attn_status_t attn_prefill_varlen_fwd(const void* q, const void* k, const void* v, void* o,
+                                      const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                                      int32_t B, int32_t H_q, int32_t H_kv, int32_t max_seqlen_q,
+                                      int32_t max_seqlen_k, int32_t total_q, int32_t total_k,
+                                      int32_t d, int32_t causal, float scale, attn_dtype_t dtype,
+                                      void* stream);
+
+/*
  * Single-query decode over a KV cache.
  *
  *   q [B,H_q,1,d], o [B,H_q,1,d]; k_cache/v_cache [B,H_kv,S_kv,d] where S_kv is

@@ -33,7 +33,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
-    assert {"attn_prefill_fwd", "attn_decode_fwd", "attn_decode_paged_fwd",
+    assert {"attn_prefill_fwd", "attn_prefill_varlen_fwd", "attn_decode_fwd", "attn_decode_paged_fwd",
             "attn_decode_workspace_bytes", "attn_status_str", "attn_last_hip_error"} <= set(names)
     for n in names:
         assert hasattr(lib, n), f"libattn.so does not export {n}"
@@ -88,6 +88,32 @@ def test_prefill_empty_is_noop(lib):
 ])
 def test_decode_rejects(lib, kw, code):
     assert decode(**kw) == code
+
+
+def prefill_varlen(q=P, k=P, v=P, o=P, cq=P, ck=P, B=2, Hq=4, Hkv=2, mq=64, mk=64, tq=100, tk=100, d=64,
+                   causal=1, scale=0.125, dtype=attn.ATTN_BF16):
+    return attn.attn_prefill_varlen_fwd(q, k, v, o, cq, ck, B, Hq, Hkv, mq, mk, tq, tk, d, causal,
+                                        scale, dtype, NULL)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=NULL), 1), (dict(o=NULL), 1), (dict(k=NULL), 1), (dict(v=NULL), 1),
+    (dict(cq=NULL), 1), (dict(ck=NULL), 1),
+    (dict(B=-1), 2), (dict(Hq=0), 2), (dict(Hq=6, Hkv=4), 2), (dict(mq=-1), 2), (dict(mk=-1), 2),
+    (dict(tq=-1), 2), (dict(tk=-5), 2), (dict(causal=3), 2),
+    (dict(mk=(1 << 20), Hkv=16, d=128), 2),                    # one sequence's K rows beyond 2^31 bytes
+    (dict(d=96), 3), (dict(dtype=attn.ATTN_F32), 3),
+    (dict(q=MIS), 4), (dict(k=MIS), 4), (dict(cq=ctypes.c_void_p(0x10002)), 4),
+    (dict(scale=math.inf), 7),
+])
+def test_prefill_varlen_rejects(lib, kw, code):
+    assert prefill_varlen(**kw) == code
+
+
+def test_prefill_varlen_empty_is_noop(lib):
+    assert prefill_varlen(q=NULL, o=NULL, tq=0) == 0
+    assert prefill_varlen(q=NULL, o=NULL, mq=0) == 0
+    assert prefill_varlen(B=0, cq=NULL, ck=NULL, q=NULL, o=NULL) == 0
 
 
 def decode_paged(q=P, kp=P, vp=P, o=P, B=2, Hq=4, Hkv=4, d=64, scale=0.125, table=P, max_blocks=4,
