@@ -31,8 +31,9 @@ attn_status_t check_common(const void* q, const void* k, const void* v, const vo
   if (B < 0 || S_q < 0 || S_kv < 0 || H_q < 1 || H_kv < 1 || d < 1) return ATTN_ERR_SHAPE;
   if (H_q % H_kv != 0) return ATTN_ERR_SHAPE;
   if (causal != 0 && causal != 1) return ATTN_ERR_SHAPE;
-  if (d != 64 && d != 128) return ATTN_ERR_UNSUPPORTED;
+  if (d != 64 && d != 128 && d != 256) return ATTN_ERR_UNSUPPORTED;
   if (dtype != ATTN_F32 && dtype != ATTN_BF16) return ATTN_ERR_UNSUPPORTED;
+  if (d == 256 && dtype != ATTN_BF16) return ATTN_ERR_UNSUPPORTED;   // d = 256: bf16 prefill only
   if (!std::isfinite(scale)) return ATTN_ERR_VALUE;
   const bool has_q = (int64_t)B * S_q > 0;
   const bool has_kv = (int64_t)B * S_kv > 0;
@@ -116,6 +117,7 @@ attn_status_t run_decode(const void* q, const void* k, const void* v, void* o, i
                          const int32_t* block_table, int32_t max_blocks, int32_t page_size,
                          int32_t num_pages) {
   if (dtype != ATTN_BF16) return ATTN_ERR_UNSUPPORTED;
+  if (d != 64 && d != 128) return ATTN_ERR_UNSUPPORTED;
   const int G = H_q / H_kv;
   if (G != 1 && G != 2 && G != 4 && G != 8 && G != 16) return ATTN_ERR_UNSUPPORTED;
   if (B == 0) return ATTN_OK;
@@ -220,7 +222,7 @@ attn_status_t attn_prefill_varlen_fwd(const void* q, const void* k, const void* 
     return ATTN_ERR_SHAPE;
   if (H_q % H_kv != 0) return ATTN_ERR_SHAPE;
   if (causal != 0 && causal != 1) return ATTN_ERR_SHAPE;
-  if (d != 64 && d != 128) return ATTN_ERR_UNSUPPORTED;
+  if (d != 64 && d != 128 && d != 256) return ATTN_ERR_UNSUPPORTED;
   if (dtype != ATTN_BF16) return ATTN_ERR_UNSUPPORTED;
   if (!std::isfinite(scale)) return ATTN_ERR_VALUE;
   const bool has_q = (int64_t)B * max_seqlen_q > 0 && total_q > 0;

@@ -9,7 +9,8 @@
 //
 // gfx950 design
 //   - 512 threads = 8 waves; each wave owns 32 query rows (256 per workgroup,
-//     one workgroup per CU at d = 128).  Large tiles halve the K/V traffic per query
+//     one workgroup per CU at d = 128).  At d = 256: 256 threads, 4 waves
+//     (one per SIMD, so a wave may use 512 registers), 128 rows.  Large tiles halve the K/V traffic per query
 //     row against 128-row tiles; the eight waves (two per SIMD) hide each
 //     other's softmax behind their matrix work.
 //   - Scores are formed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16:
@@ -60,20 +61,31 @@ namespace attn {
 
 namespace {
 
-constexpr int kRows = 256;   // query rows per workgroup
 constexpr int kKeys = 64;    // keys per compute block
-constexpr int kStage = 128;  // keys per LDS stage (two compute blocks)
-constexpr int kThreads = 512;
 constexpr int kXcds = 8;                      // accelerator complex dies of an MI355X
 constexpr float kRescaleSlack = 8.f;   // base-2 headroom before the accumulator is rescaled
 
+// Workgroup shape per head dimension.  d = 64, 128: 8 waves (two per SIMD),
+// 256 query rows, 128-key LDS stages (two compute blocks).  d = 256: the
+// output accumulator alone takes 128 registers per lane, so 4 waves (one per
+// SIMD, up to 512 registers), 128 rows and 64-key stages.
+template <int D>
+struct Cfg {
+  static constexpr int kThreads = D == 256 ? 256 : 512;
+  static constexpr int kWaves = kThreads / 64;
+  static constexpr int kRows = kWaves * 32;               // query rows per workgroup
+  static constexpr int kStage = D == 256 ? 64 : 128;      // keys per LDS stage
+  static constexpr int kBlocksPerStage = kStage / kKeys;
+};
+
 template <int D>
 struct Tile {
+  static constexpr int kStage = Cfg<D>::kStage;
   static constexpr int kSlots = D / 8;                    // 16-byte slots per row
   static constexpr int kRowBytes = D * 2;
   static constexpr int kBytes = kStage * kRowBytes;       // one K or V stage
   static constexpr int kSubBytes = kKeys * kRowBytes;     // one compute block inside it
-  static constexpr int kPiecesPerThread = kStage * kSlots / kThreads;
+  static constexpr int kPiecesPerThread = kStage * kSlots / Cfg<D>::kThreads;
   // Swizzle of row r: its 16-byte slot s is stored at slot s ^ sw(r).  With
   // gfx950's 64 four-byte LDS banks (a row of 16 slots spans them all once)
   // two access patterns must hit distinct banks: the K-operand read (16
@@ -81,8 +93,11 @@ struct Tile {
   // the transpose read of V (4 rows aligned to 4, 4 consecutive slots each:
   // the rows' slot quads must not overlap).  For 8-slot rows (d = 64) two
   // rows share the 64 banks, so the same holds within even and odd rows.
+  // 32-slot rows (d = 256) span the banks twice; slot s and s + 16 share
+  // banks, and the 16-slot permutation (which never moves a slot across
+  // that boundary) keeps both patterns conflict-free.
   __device__ static __forceinline__ int sw(int r) {
-    if (kSlots == 16) return ((r & 3) << 2) | ((r >> 2) & 3);
+    if (kSlots >= 16) return ((r & 3) << 2) | ((r >> 2) & 3);
     return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
   }
   // byte offset of (row, 16-byte slot) inside a swizzled block
@@ -96,8 +111,12 @@ struct Tile {
 // registers so two workgroups share a CU (four waves per SIMD; its LDS
 // stages take 64 KiB); the other variants run one workgroup per CU.
 template <int D, bool CAUSAL, bool POS>
-__global__ __launch_bounds__(kThreads, (D == 64 && CAUSAL) ? 4 : 1) void prefill_bf16_kernel(PrefillParams p) {
+__global__ __launch_bounds__(Cfg<D>::kThreads, (D == 64 && CAUSAL) ? 4 : 1) void prefill_bf16_kernel(PrefillParams p) {
   using T = Tile<D>;
+  constexpr int kThreads = Cfg<D>::kThreads;
+  constexpr int kRows = Cfg<D>::kRows;
+  constexpr int kStage = Cfg<D>::kStage;
+  constexpr int BPS = Cfg<D>::kBlocksPerStage;
   constexpr int KS = D / 16;       // k-steps of the score MFMA (16 features each)
   constexpr int DT = D / 32;       // 32-feature output tiles
   constexpr int NP = T::kPiecesPerThread;
@@ -202,17 +221,22 @@ __global__ __launch_bounds__(kThreads, (D == 64 && CAUSAL) ? 4 : 1) void prefill
   }
 
   // Staging by direct global -> LDS copies.  Copy u of wave w fills the
-  // 1 KiB LDS chunk c = u*8 + w of a stage; lane i lands at byte 16*i of
-  // it, i.e. at (row, physical slot), and so fetches logical slot
-  // physical ^ swizzle(row) of that row.  Rows per pass are a multiple of 16,
-  // so the swizzle, and hence the lane's byte offset, only shift by a
-  // constant from one copy to the next.
+  // 1 KiB LDS chunk c = u*kWaves + w of a stage; lane i lands at byte 16*i
+  // of it, i.e. at (row, physical slot), and so fetches logical slot
+  // physical ^ swizzle(row) of that row.  When the rows a copy round covers
+  // are a multiple of 16 (d = 64, 128) the swizzle repeats from one copy to
+  // the next and one lane offset serves all; otherwise (d = 256: 8 rows per
+  // round) each copy has its own slot.
   constexpr int kPassBytes = kThreads * 16;                 // one copy round of all waves
   constexpr int kPassRows = kPassBytes / T::kRowBytes;      // key rows it covers
+  constexpr bool kSameSlot = kPassRows % 16 == 0;
   const int st_byte0 = wave * 1024 + lane * 16;             // LDS byte of copy 0
   const int st_row0 = st_byte0 / T::kRowBytes;
-  const int st_slot0 = (st_byte0 % T::kRowBytes) / 16 ^ T::sw(st_row0);
-  const uint32_t g_off0 = (uint32_t)(st_row0 * kv_row_bytes + st_slot0 * 16);
+  const int st_phys = (st_byte0 % T::kRowBytes) / 16;       // physical slot (same for every copy)
+  int st_slot[kSameSlot ? 1 : NP];                          // logical slot of copy u
+#pragma unroll
+  for (int u = 0; u < (kSameSlot ? 1 : NP); ++u) st_slot[u] = st_phys ^ T::sw(st_row0 + u * kPassRows);
+  auto slot_of = [&](int u) { return kSameSlot ? st_slot[0] : st_slot[u]; };
   uint32_t k_off[KS];                       // K operand (row col; row col+32 adds a constant)
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) k_off[ks] = T::off(col, 2 * ks + half);
@@ -243,7 +267,7 @@ __global__ __launch_bounds__(kThreads, (D == 64 && CAUSAL) ? 4 : 1) void prefill
     if constexpr (decltype(stage_c)::value == 0) return v_s0; else return v_s1;
   };
 
-  // Copy 128 keys of K (or V) into an LDS stage.  Rows past n are clamped
+  // Copy one stage of K (or V) into LDS.  Rows past n are clamped
   // to row n-1 (only in the last stage) so no byte beyond a sequence is read.
   // one head's rows of this sequence: (n - 1) strides plus one row
   const int kv_bytes = n > 0 ? (n - 1) * kv_row_bytes + T::kRowBytes : 0;
@@ -255,12 +279,13 @@ __global__ __launch_bounds__(kThreads, (D == 64 && CAUSAL) ? 4 : 1) void prefill
     if (j0 + kStage <= n) {
 #pragma unroll
       for (int u = 0; u < NP; ++u)
-        buffer_to_lds16(rsrc, d + u * kPassBytes, (int)g_off0, (j0 + u * kPassRows) * kv_row_bytes);
+        buffer_to_lds16(rsrc, d + u * kPassBytes, st_row0 * kv_row_bytes + slot_of(u) * 16,
+                        (j0 + u * kPassRows) * kv_row_bytes);
     } else {
 #pragma unroll
       for (int u = 0; u < NP; ++u) {
         const int row = st_row0 + u * kPassRows;
-        buffer_to_lds16(rsrc, d + u * kPassBytes, min(j0 + row, n - 1) * kv_row_bytes + st_slot0 * 16, 0);
+        buffer_to_lds16(rsrc, d + u * kPassBytes, min(j0 + row, n - 1) * kv_row_bytes + slot_of(u) * 16, 0);
       }
     }
   };
@@ -382,11 +407,11 @@ __global__ __launch_bounds__(kThreads, (D == 64 && CAUSAL) ? 4 : 1) void prefill
   };
 
   // ---- the key loop ------------------------------------------------------
-  // An LDS stage holds 128 keys, processed as two 64-key compute blocks; the
-  // copies of the next stage are issued between the two blocks (the other
-  // buffer was last read in the previous stage, closed by its barrier), and
-  // one barrier closes the stage.
-  const int n_stages = (n_blocks + 1) / 2;
+  // An LDS stage holds BPS 64-key compute blocks.  The copies of the next
+  // stage go to the other buffer, last read in the previous stage (closed by
+  // its barrier): with two blocks per stage they are issued between them,
+  // with one block before it.  One barrier closes the stage.
+  const int n_stages = (n_blocks + BPS - 1) / BPS;
   auto block = [&](auto st_c, auto sub_c, int blk) {
     if (active(blk)) {
       f32x16 sc[2];
@@ -405,13 +430,21 @@ __global__ __launch_bounds__(kThreads, (D == 64 && CAUSAL) ? 4 : 1) void prefill
   };
   auto stage_step = [&](auto st_c, int sb) {
     using Sn = std::integral_constant<int, 1 - decltype(st_c)::value>;
-    block(st_c, std::integral_constant<int, 0>{}, 2 * sb);
-    __builtin_amdgcn_sched_barrier(0);
-    if (sb + 1 < n_stages) {
-      load_k(Sn{}, (sb + 1) * kStage);
-      load_v(Sn{}, (sb + 1) * kStage);
+    if constexpr (BPS == 1) {
+      if (sb + 1 < n_stages) {
+        load_k(Sn{}, (sb + 1) * kStage);
+        load_v(Sn{}, (sb + 1) * kStage);
+      }
+      block(st_c, std::integral_constant<int, 0>{}, sb);
+    } else {
+      block(st_c, std::integral_constant<int, 0>{}, 2 * sb);
+      __builtin_amdgcn_sched_barrier(0);
+      if (sb + 1 < n_stages) {
+        load_k(Sn{}, (sb + 1) * kStage);
+        load_v(Sn{}, (sb + 1) * kStage);
+      }
+      if (2 * sb + 1 < n_blocks) block(st_c, std::integral_constant<int, 1>{}, 2 * sb + 1);
     }
-    if (2 * sb + 1 < n_blocks) block(st_c, std::integral_constant<int, 1>{}, 2 * sb + 1);
     __builtin_amdgcn_sched_barrier(0);
     wait_vmem();
     __syncthreads();
@@ -449,13 +482,14 @@ __global__ __launch_bounds__(kThreads, (D == 64 && CAUSAL) ? 4 : 1) void prefill
 
 template <int D, bool CAUSAL>
 hipError_t launch(const PrefillParams& p, hipStream_t stream) {
-  const int n_qt = (p.Sq + kRows - 1) / kRows;
+  const int n_qt = (p.Sq + Cfg<D>::kRows - 1) / Cfg<D>::kRows;
   const int n_pr = CAUSAL ? (n_qt + 1) / 2 : n_qt;
   dim3 grid((unsigned)n_pr * p.Hq * p.B);
+  const dim3 block(Cfg<D>::kThreads);
   if (p.scale_log2 >= 0.f)
-    hipLaunchKernelGGL((prefill_bf16_kernel<D, CAUSAL, true>), grid, dim3(kThreads), 0, stream, p);
+    hipLaunchKernelGGL((prefill_bf16_kernel<D, CAUSAL, true>), grid, block, 0, stream, p);
   else
-    hipLaunchKernelGGL((prefill_bf16_kernel<D, CAUSAL, false>), grid, dim3(kThreads), 0, stream, p);
+    hipLaunchKernelGGL((prefill_bf16_kernel<D, CAUSAL, false>), grid, block, 0, stream, p);
   return hipGetLastError();
 }
 
@@ -463,6 +497,7 @@ hipError_t launch(const PrefillParams& p, hipStream_t stream) {
 
 hipError_t launch_prefill_bf16(const PrefillParams& p, hipStream_t stream) {
   if (p.d == 64) return p.causal ? launch<64, true>(p, stream) : launch<64, false>(p, stream);
+  if (p.d == 256) return p.causal ? launch<256, true>(p, stream) : launch<256, false>(p, stream);
   return p.causal ? launch<128, true>(p, stream) : launch<128, false>(p, stream);
 }
 

@@ -71,6 +71,8 @@ WORKLOADS = [
              True, k_mult=4.0, note="long causal GQA prefill, K scaled by 4"),
     Workload("prefill_bf16_b4h32s4096_d64", "prefill", 4, 32, 32, 4096, 4096, 64, "bf16", True,
              note="causal prefill at head dimension 64"),
+    Workload("prefill_bf16_b4h16s4096_d256", "prefill", 4, 16, 16, 4096, 4096, 256, "bf16", True,
+             note="causal prefill at head dimension 256 (the headline's FLOPs with half the heads)"),
     Workload("prefill_chunked_gqa_bf16_b16h32kv8q512", "prefill", 16, 32, 8, 512, 8192, 128,
              "bf16", True, len_range=(512, 8192),
              note="chunked prefill: 512 new tokens per sequence over a ragged KV cache "

@@ -73,7 +73,7 @@ typedef enum {
  *   B >= 0, S_q >= 0, S_kv >= 0, H_q >= 1, H_kv >= 1, H_q % H_kv == 0.
  *   One head's rows (S_q*d or S_kv*d elements) span at most 2^31 - 1 bytes
  *   (else ATTN_ERR_SHAPE).
- *   d: 64 or 128.
+ *   d: 64 or 128, and 256 with ATTN_BF16 (else ATTN_ERR_UNSUPPORTED).
  *   causal: 0 or 1; causal with S_q > S_kv is rejected (ATTN_ERR_SHAPE).
  *   scale: finite; the usual value is 1/sqrt(d).
  *   kv_lens: see above.
@@ -103,7 +103,7 @@ attn_status_t attn_prefill_fwd(const void* q, const void* k, const void* v, void
  *   causal: bottom-right per sequence (query i of a sequence with s queries
  *   and n keys sees key j iff j <= i + n - s); a row that sees no key, also
  *   every row of a sequence with n = 0, gets O = 0.
- *   d: 64 or 128; dtype: ATTN_BF16 only (else ATTN_ERR_UNSUPPORTED).
+ *   d: 64, 128 or 256; dtype: ATTN_BF16 only (else ATTN_ERR_UNSUPPORTED).
  *   max_seqlen_k * H_kv * d * 2 <= 2^31 - 1 (else ATTN_ERR_SHAPE).
  *   cu_seqlens_* must be 4-byte aligned, the tensors 16-byte aligned.
  *

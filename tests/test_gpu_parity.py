@@ -65,6 +65,11 @@ PREFILL_CASES = [
     (1, 16, 8, 530, 530, 64, True, None, "bf16"),
     (1, 8, 8, 700, 640, 128, False, [640], "bf16"),
     (2, 8, 2, 520, 777, 128, True, [777, 300], "bf16"),
+    # d = 256 (four waves, 128-row tiles, 64-key stages)
+    (2, 4, 2, 300, 300, 256, True, None, "bf16"),
+    (1, 4, 4, 200, 330, 256, False, [330], "bf16"),
+    (1, 8, 8, 600, 600, 256, True, None, "bf16"),
+    (2, 4, 1, 130, 700, 256, True, [700, 257], "bf16"),
     # causal tile pairs: five tiles (a middle tile alone), four tiles at d = 64
     (1, 4, 2, 1100, 1100, 128, True, None, "bf16"),
     (1, 8, 8, 1024, 1024, 64, True, None, "bf16"),
@@ -322,7 +327,7 @@ def test_side_stream_ordering():
 # full-size workloads: sampled rows against the oracle + whole-output checks
 # ---------------------------------------------------------------------------
 @pytest.mark.parametrize("name", ["prefill_bf16_b4h32s4096", "prefill_gqa_bf16_h64kv8s16384",
-                                  "prefill_bf16_b4h32s4096_d64",
+                                  "prefill_bf16_b4h32s4096_d64", "prefill_bf16_b4h16s4096_d256",
                                   "prefill_chunked_gqa_bf16_b16h32kv8q512"])
 def test_prefill_workload_sampled(name):
     w = wl.BY_NAME[name]

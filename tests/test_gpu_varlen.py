@@ -20,6 +20,7 @@ CASES = [
     (4, 4, 64, True, [1, 257, 640], [1, 257, 900]),
     (8, 1, 128, False, [77, 512, 3], [700, 64, 3]),
     (4, 2, 128, True, [200, 100], [0, 150]),                # a sequence with no key at all
+    (4, 2, 256, True, [300, 129, 1], [400, 129, 2]),         # d = 256
 ]
 
 
