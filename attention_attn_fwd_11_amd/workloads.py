@@ -219,3 +219,14 @@ def varlen_flops(Hq, d, q_lens, k_lens, causal=True):
         else:
             pairs += s * n
     return 4 * d * Hq * pairs
+
+
+def rope_table(rows, d, theta=10000.0, device="cpu"):
+    """Rotary-embedding table [rows, d] float32: columns f < d/2 hold
+    cos(p * theta^(-2f/d)), columns d/2 + f the matching sin, for positions
+    p = 0 .. rows-1 (computed in float64, stored as float32).  An input like
+    Q, K and V: both the kernels and the oracle read these values."""
+    h = d // 2
+    inv = theta ** (-2.0 * torch.arange(h, dtype=torch.float64) / d)
+    ang = torch.arange(rows, dtype=torch.float64)[:, None] * inv[None, :]
+    return torch.cat([ang.cos(), ang.sin()], dim=1).to(torch.float32).to(device)
