@@ -134,8 +134,10 @@ def attention(q, k, v, causal, scale, kv_lens=None, want_lse=False, want_p=False
 def attention_rows(q, k, v, causal, scale, rows, kv_lens=None, want_lse=False, lib=None):
     """fp64 attention for selected (b, h_q, i) rows.  Returns o [n, d] (and lse [n])."""
     qa, dt = _as_stored(q)
-    ka, _ = _as_stored(k)
-    va, _ = _as_stored(v)
+    ka, dtk = _as_stored(k)
+    va, dtv = _as_stored(v)
+    if not (dt == dtk == dtv):
+        raise TypeError("q, k, v must share one dtype")
     B, Hq, Hkv, Sq, Skv, d = _shapes(qa, ka, va)
     lens = _lens(kv_lens, B)
     sel = np.ascontiguousarray(np.asarray(rows, dtype=np.int64).reshape(-1, 3))
