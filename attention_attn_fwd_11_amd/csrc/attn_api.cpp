@@ -210,6 +210,34 @@ attn_status_t attn_prefill_fwd(const void* q, const void* k, const void* v, void
   return e == hipSuccess ? ATTN_OK : hip_fail("prefill launch", e);
 }
 
+attn_status_t attn_prefill_rope_fwd(const void* q, const void* k, const void* v, void* o, int32_t B,
+                                    int32_t H_q, int32_t H_kv, int32_t S_q, int32_t S_kv, int32_t d,
+                                    int32_t causal, float scale, const int32_t* kv_lens,
+                                    const float* rope_table, int32_t rope_rows, attn_dtype_t dtype,
+                                    void* stream) {
+  g_hip_error[0] = '\0';
+  attn_status_t st = check_common(q, k, v, o, B, H_q, H_kv, S_q, S_kv, d, causal, scale, dtype);
+  if (st != ATTN_OK) return st;
+  if (dtype != ATTN_BF16) return ATTN_ERR_UNSUPPORTED;
+  if (causal && S_q > S_kv) return ATTN_ERR_SHAPE;
+  if (rope_rows < S_kv || rope_rows < 1) return ATTN_ERR_SHAPE;   // every key position has a row
+  if ((int64_t)B * S_q > 0 && S_kv > 0 && !rope_table) return ATTN_ERR_NULL;
+  if (rope_table && !aligned16(rope_table)) return ATTN_ERR_ALIGN;
+  if ((int64_t)B * S_q == 0) return ATTN_OK;  // nothing to compute
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (S_kv == 0) {
+    hipError_t e = attn::launch_zero_fill(o, (size_t)B * H_q * S_q * d * 2, s);
+    return e == hipSuccess ? ATTN_OK : hip_fail("zero-fill launch", e);
+  }
+  attn::PrefillParams p{};
+  p.q = q; p.k = k; p.v = v; p.o = o; p.kv_lens = kv_lens;
+  p.B = B; p.Hq = H_q; p.Hkv = H_kv; p.Sq = S_q; p.Skv = S_kv; p.d = d; p.causal = causal;
+  p.scale_log2 = (float)((double)scale * 1.4426950408889634);
+  p.rope = rope_table; p.rope_rows = rope_rows;
+  hipError_t e = attn::launch_prefill_bf16(p, s);
+  return e == hipSuccess ? ATTN_OK : hip_fail("prefill launch", e);
+}
+
 attn_status_t attn_prefill_varlen_fwd(const void* q, const void* k, const void* v, void* o,
                                       const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
                                       int32_t B, int32_t H_q, int32_t H_kv, int32_t max_seqlen_q,

@@ -24,6 +24,11 @@ struct PrefillParams {
   const int32_t* cu_q;
   const int32_t* cu_k;
   int total_q, total_k;
+  // Rotary embedding (rope != nullptr, bf16 only): table [rope_rows, d] fp32,
+  // columns f < d/2 the cos and d/2 + f the sin of position p's angle for
+  // frequency f; Q and K are rotated (rotate-half pairs) before the scores.
+  const float* rope;
+  int rope_rows;
 };
 
 struct DecodeParams {

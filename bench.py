@@ -195,6 +195,29 @@ def varlen_prefill(torch, attn, wl, dev, steps, warmup):
             "algorithmic_flop": fl, "tokens": sum(lens)}
 
 
+def rope_prefill(torch, attn, wl, x, w, steps, warmup):
+    """The headline causal prefill with the rotary embedding fused in (Q and
+    K rotated inside the kernel from a [S, d] fp32 cos/sin table).  The
+    rotation adds no MFMA work: the rate counts the same attention FLOPs."""
+    table = wl.rope_table(w.Skv, w.d, device=x["q"].device)
+    out = torch.empty_like(x["q"])
+    f = lambda: attn.prefill(x["q"], x["k"], x["v"], causal=w.causal, scale=w.scale, out=out,
+                             rope=table)
+    for _ in range(warmup):
+        f()
+    torch.cuda.synchronize()
+    tm = Timer(torch)
+    for _ in range(steps):
+        tm(f)
+    torch.cuda.synchronize()
+    ms, _ = tm.mean_ms()
+    fl = wl.prefill_flops(w)
+    return {"shape": w.describe() + " + fused RoPE", "ms": round(ms, 4),
+            "TFLOP/s": round(fl / (ms * 1e-3) / 1e12, 1),
+            "frac_of_mfma_peak": round(fl / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+            "algorithmic_flop": fl}
+
+
 def paged_decode(torch, attn, wl, x, w, steps, warmup, page_size=128):
     """The ragged GQA decode with its cache in page_size-key pages (only the
     pages the lengths need, in shuffled order); same algorithmic bytes as the
@@ -427,6 +450,8 @@ def main():
         other["decode_paged_gqa_bf16_b128h32kv8_p128"] = paged_decode(
             torch, attn, wl, inputs[wg.name], wg, args.steps, args.warmup)
         other[wl.VARLEN.name] = varlen_prefill(torch, attn, wl, dev, args.steps, args.warmup)
+        other["prefill_rope_bf16_b4h32s4096"] = rope_prefill(torch, attn, wl, inputs[wp.name], wp,
+                                                             args.steps, args.warmup)
     other["decode_graph_small"] = decode_graph(torch, attn, wl, dev)
     probe = read_probe(torch, dev)
     out["context"] = {

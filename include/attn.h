@@ -91,6 +91,30 @@ attn_status_t attn_prefill_fwd(const void* q, const void* k, const void* v, void
                                attn_dtype_t dtype, void* stream);
 
 /*
+ * Attention forward with the rotary position embedding fused in (bf16).
+ *
+ *   Arguments as attn_prefill_fwd (dtype ATTN_BF16 only, else
+ *   ATTN_ERR_UNSUPPORTED), plus
+ *   rope_table: device fp32 [rope_rows, d], 16-byte aligned; row p holds
+ *   cos(p * theta_f) in column f and sin(p * theta_f) in column d/2 + f for
+ *   f < d/2.  rope_rows >= S_kv (else ATTN_ERR_SHAPE).
+ * Each query and key row x at position p becomes
+ *   (x[f] cos - x[f + d/2] sin, x[f + d/2] cos + x[f] sin),  f < d/2,
+ * in fp32, rounded to bf16, before the scores.  Key j is at position j;
+ * query i of a sequence with n keys at n - S_q + i (the causal mask's
+ * bottom-right alignment; rows that see no key use position 0).  V is not
+ * rotated.  RoPE is the step "GPU learning day 24: Operator Fusion",
+ * section 6 (exercise 1's reference answer), places inside the attention
+ * kernel; the pages give no formula, and this is the rotate-half form.
+ * Keys are rotated once per workgroup in LDS as each K stage arrives.
+ */
+attn_status_t attn_prefill_rope_fwd(const void* q, const void* k, const void* v, void* o, int32_t B,
+                                    int32_t H_q, int32_t H_kv, int32_t S_q, int32_t S_kv, int32_t d,
+                                    int32_t causal, float scale, const int32_t* kv_lens,
+                                    const float* rope_table, int32_t rope_rows, attn_dtype_t dtype,
+                                    void* stream);
+
+/*
  * Attention forward over packed variable-length sequences (bf16).
  *
  *   q [total_q, H_q, d], o [total_q, H_q, d]; k, v [total_k, H_kv, d]

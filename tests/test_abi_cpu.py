@@ -33,7 +33,8 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
-    assert {"attn_prefill_fwd", "attn_prefill_varlen_fwd", "attn_decode_fwd", "attn_decode_paged_fwd",
+    assert {"attn_prefill_fwd", "attn_prefill_rope_fwd", "attn_prefill_varlen_fwd", "attn_decode_fwd",
+            "attn_decode_paged_fwd",
             "attn_decode_workspace_bytes", "attn_status_str", "attn_last_hip_error"} <= set(names)
     for n in names:
         assert hasattr(lib, n), f"libattn.so does not export {n}"
@@ -89,6 +90,23 @@ def test_prefill_empty_is_noop(lib):
 ])
 def test_decode_rejects(lib, kw, code):
     assert decode(**kw) == code
+
+
+def prefill_rope(q=P, k=P, v=P, o=P, B=1, Hq=2, Hkv=2, Sq=8, Skv=8, d=64, causal=1, scale=0.125,
+                 lens=NULL, table=P, rows=8, dtype=attn.ATTN_BF16):
+    return attn.attn_prefill_rope_fwd(q, k, v, o, B, Hq, Hkv, Sq, Skv, d, causal, scale, lens, table,
+                                      rows, dtype, NULL)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=NULL), 1), (dict(k=NULL), 1), (dict(table=NULL), 1),
+    (dict(rows=7), 2), (dict(rows=0), 2), (dict(Sq=9, Skv=8), 2), (dict(Hq=6, Hkv=4), 2),
+    (dict(dtype=attn.ATTN_F32), 3), (dict(d=96), 3),
+    (dict(table=MIS), 4), (dict(q=MIS), 4),
+    (dict(scale=math.nan), 7),
+])
+def test_prefill_rope_rejects(lib, kw, code):
+    assert prefill_rope(**kw) == code
 
 
 def prefill_varlen(q=P, k=P, v=P, o=P, cq=P, ck=P, B=2, Hq=4, Hkv=2, mq=64, mk=64, tq=100, tk=100, d=64,

@@ -1,0 +1,109 @@
+"""Prefill with the rotary embedding fused in (attn_prefill_rope_fwd) against
+the fp64 oracle that rotates Q and K first (oracle.rope), plus two
+properties: an identity table (cos 1, sin 0) gives exactly the plain
+prefill's output, and a table of random rotations applied to Q and K on the
+host before a plain prefill gives the same scores up to bf16 rounding."""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import attention_attn_fwd_11_amd as attn
+import oracle
+from attention_attn_fwd_11_amd import workloads as wl
+from oracle import rope as orope
+from tests.gpu_util import assert_close, convex_bound_ok, sample_rows
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+CASES = [
+    # B, Hq, Hkv, Sq, Skv, d, causal, kv_lens, extra table rows
+    (2, 4, 2, 300, 300, 128, True, None, 0),
+    (1, 4, 4, 700, 700, 64, True, None, 5),
+    (2, 4, 1, 129, 1000, 128, True, None, 0),          # chunk of queries at the end of the keys
+    (2, 2, 2, 200, 333, 128, False, None, 17),
+    (3, 4, 2, 256, 600, 128, True, [600, 1, 300], 0),   # ragged KV lengths
+    (2, 4, 2, 300, 300, 256, True, None, 0),
+    (1, 2, 2, 100, 450, 256, False, [450], 3),
+    (2, 4, 4, 64, 64, 64, False, [64, 0], 0),           # a sequence with no key
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: f"B{c[0]}H{c[1]}-{c[2]}-q{c[3]}k{c[4]}-d{c[5]}"
+                                                    f"-c{int(c[6])}-l{int(c[7] is not None)}")
+def test_rope_prefill_matches_oracle(case):
+    B, Hq, Hkv, Sq, Skv, d, causal, lens, spare = case
+    say(f"rope prefill {case}")
+    x = wl.random_problem(B, Hq, Hkv, Sq, Skv, d, dtype="bf16", device=DEV, seed=41)
+    table = wl.rope_table(Skv + spare, d, device=DEV)
+    scale = 1.0 / np.sqrt(d)
+    lens_t = None if lens is None else torch.tensor(lens, dtype=torch.int32, device=DEV)
+    o = attn.prefill(x["q"], x["k"], x["v"], causal=causal, scale=scale, kv_lens=lens_t, rope=table)
+    torch.cuda.synchronize()
+    ref = orope.attention_rope(x["q"].cpu(), x["k"].cpu(), x["v"].cpu(), causal, scale, table.cpu(),
+                               kv_lens=lens)
+    assert_close(o, ref, torch.bfloat16, f"rope prefill {case}")
+
+
+@pytest.mark.parametrize("d", [64, 128, 256])
+def test_identity_table_equals_plain_prefill(d):
+    say(f"rope identity table d{d}")
+    B, Hq, Hkv, S = 2, 4, 2, 333
+    x = wl.random_problem(B, Hq, Hkv, S, S, d, dtype="bf16", device=DEV, seed=42)
+    table = torch.cat([torch.ones(S, d // 2), torch.zeros(S, d // 2)], dim=1).to(DEV)
+    a = attn.prefill(x["q"], x["k"], x["v"], causal=True, rope=table)
+    b = attn.prefill(x["q"], x["k"], x["v"], causal=True)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b), "cos 1 / sin 0 must leave Q and K unchanged"
+
+
+def test_rope_equals_host_rotation_then_plain_prefill():
+    """Rotating Q and K on the host (fp64, rounded to bf16 once) and then
+    running the plain prefill must agree with the fused path to bf16
+    rounding: the fused path rounds the same rotated values once too."""
+    say("rope vs host rotation")
+    B, Hq, Hkv, S, d = 1, 4, 2, 520, 128
+    x = wl.random_problem(B, Hq, Hkv, S, S, d, dtype="bf16", device=DEV, seed=43)
+    table = wl.rope_table(S, d, theta=500.0, device=DEV)
+    pos = np.arange(S)
+    qr = torch.from_numpy(orope.rope(x["q"].cpu(), table.cpu(), pos)).to(torch.bfloat16).to(DEV)
+    kr = torch.from_numpy(orope.rope(x["k"].cpu(), table.cpu(), pos)).to(torch.bfloat16).to(DEV)
+    fused = attn.prefill(x["q"], x["k"], x["v"], causal=True, rope=table)
+    host = attn.prefill(qr, kr, x["v"], causal=True)
+    torch.cuda.synchronize()
+    diff = (fused.float() - host.float()).abs()
+    assert float(diff.max()) <= 1e-2 and float(diff.mean()) <= 1e-3, \
+        f"fused vs host rotation: max {float(diff.max()):.3e} mean {float(diff.mean()):.3e}"
+
+
+def test_rope_workload_sampled():
+    """The headline causal shape (B 4, H 32, S 4096, d 128) with RoPE:
+    sampled rows against the oracle, whole output inside V's convex hull."""
+    w = wl.BY_NAME["prefill_bf16_b4h32s4096"]
+    say(f"rope workload: {w.describe()}")
+    x = wl.generate(w, DEV)
+    table = wl.rope_table(w.Skv, w.d, device=DEV)
+    o = attn.prefill(x["q"], x["k"], x["v"], causal=True, scale=w.scale, rope=table)
+    torch.cuda.synchronize()
+    ok, finite = convex_bound_ok(o, x["v"], w.Hq)
+    assert finite and ok, "output outside the convex hull of V"
+    S = w.Sq
+    rows = sample_rows(w.B, w.Hq, S, 120, seed=2, extra=[(0, 0, 0), (w.B - 1, w.Hq - 1, S - 1),
+                                                          (1, 5, 255), (2, 7, 256)])
+    pos = np.arange(S)
+    tc = table.cpu()
+    qr = orope.rope(x["q"].cpu(), tc, pos)
+    kr = orope.rope(x["k"].cpu(), tc, pos)
+    ref = oracle.attention_rows(qr, kr, x["v"].cpu().double(), True, w.scale, rows)
+    idx = torch.tensor(rows, dtype=torch.long)
+    got = o[idx[:, 0], idx[:, 1], idx[:, 2]]
+    assert_close(got, ref, torch.bfloat16, "rope headline sampled rows")
