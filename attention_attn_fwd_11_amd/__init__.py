@@ -19,7 +19,7 @@ import torch
 __all__ = [
     "ATTN_F32", "ATTN_BF16", "AttnError", "attn_prefill_fwd", "attn_decode_fwd",
     "attn_decode_paged_fwd", "attn_prefill_varlen_fwd", "attn_prefill_rope_fwd",
-    "attn_decode_workspace_bytes",
+    "attn_prefill_rope_workspace_bytes", "attn_decode_workspace_bytes",
     "attn_status_str", "attn_last_hip_error", "prefill", "prefill_varlen", "decode",
     "decode_paged", "library_path",
 ]
@@ -60,7 +60,9 @@ def _load():
                                                 i32, i32, i32, f32, ctypes.c_int, vp]
         lib.attn_prefill_varlen_fwd.restype = ctypes.c_int
         lib.attn_prefill_rope_fwd.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, f32,
-                                              vp, vp, i32, ctypes.c_int, vp]
+                                              vp, vp, i32, vp, ctypes.c_size_t, ctypes.c_int, vp]
+        lib.attn_prefill_rope_workspace_bytes.argtypes = [i32, i32, i32, i32]
+        lib.attn_prefill_rope_workspace_bytes.restype = ctypes.c_size_t
         lib.attn_prefill_rope_fwd.restype = ctypes.c_int
         lib.attn_decode_paged_fwd.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, f32, vp, i32, i32,
                                               i32, vp, ctypes.c_int, vp, sz, vp]
@@ -84,9 +86,14 @@ def attn_prefill_fwd(q, k, v, o, B, H_q, H_kv, S_q, S_kv, d, causal, scale, kv_l
 
 
 def attn_prefill_rope_fwd(q, k, v, o, B, H_q, H_kv, S_q, S_kv, d, causal, scale, kv_lens, rope_table,
-                          rope_rows, dtype, stream):
+                          rope_rows, workspace, workspace_bytes, dtype, stream):
     return _load().attn_prefill_rope_fwd(q, k, v, o, B, H_q, H_kv, S_q, S_kv, d, causal, scale,
-                                         kv_lens, rope_table, rope_rows, dtype, stream)
+                                         kv_lens, rope_table, rope_rows, workspace, workspace_bytes,
+                                         dtype, stream)
+
+
+def attn_prefill_rope_workspace_bytes(B, H_kv, S_kv, d):
+    return _load().attn_prefill_rope_workspace_bytes(B, H_kv, S_kv, d)
 
 
 def attn_prefill_varlen_fwd(q, k, v, o, cu_seqlens_q, cu_seqlens_k, B, H_q, H_kv, max_seqlen_q,
@@ -161,12 +168,14 @@ def _lens(kv_lens, B, device):
     return kv_lens
 
 
-def prefill(q, k, v, causal=True, scale=None, kv_lens=None, out=None, rope=None):
+def prefill(q, k, v, causal=True, scale=None, kv_lens=None, out=None, rope=None, rope_workspace=None):
     """Attention forward.  q [B,H_q,S_q,d]; k, v [B,H_kv,S_kv,d]; fp32 or bf16.
 
     Returns o [B,H_q,S_q,d] with q's dtype.  kv_lens (optional) is int32 [B]
     on the device.  rope (optional, bf16 only): fp32 [rows, d] cos/sin table;
-    Q and K are then rotated inside the kernel (attn_prefill_rope_fwd).
+    Q and K are then rotated (attn_prefill_rope_fwd): K inside the kernel,
+    or, with rope_workspace (a uint8 device tensor of at least
+    attn_prefill_rope_workspace_bytes bytes), once into that buffer first.
     Runs on torch's current stream for q's device.
     """
     if q.dtype not in _DTYPES:
@@ -193,9 +202,15 @@ def prefill(q, k, v, causal=True, scale=None, kv_lens=None, out=None, rope=None)
         _check_tensor("rope", rope, torch.float32)
         if rope.dim() != 2 or rope.shape[1] != d or rope.device != q.device:
             raise ValueError("rope must be float32 [rows, d] on q's device")
+        ws, ws_bytes = None, 0
+        if rope_workspace is not None:
+            if not rope_workspace.is_cuda or rope_workspace.device != q.device:
+                raise ValueError("rope_workspace must be on q's device")
+            ws, ws_bytes = _ptr(rope_workspace), rope_workspace.numel() * rope_workspace.element_size()
         st = attn_prefill_rope_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), B, H_q, H_kv, S_q, S_kv, d,
                                    int(bool(causal)), float(scale), _ptr(lens), _ptr(rope),
-                                   rope.shape[0], _DTYPES[q.dtype], ctypes.c_void_p(stream))
+                                   rope.shape[0], ws, ws_bytes, _DTYPES[q.dtype],
+                                   ctypes.c_void_p(stream))
         if st != 0:
             raise AttnError(st, "attn_prefill_rope_fwd")
         return o

@@ -19,7 +19,8 @@ LIB = os.path.join(PKG, "libattn.so")
 PROBE_LIB = os.path.join(PKG, "libattn_probe.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["attn_api.cpp", "prefill_f32.hip", "prefill_bf16.hip", "decode_bf16.hip", "util.hip"]
+SOURCES = ["attn_api.cpp", "prefill_f32.hip", "prefill_bf16.hip", "decode_bf16.hip", "util.hip",
+           "rope_bf16.hip"]
 PROBE_SOURCES = ["read_probe.hip"]
 
 # Device code for gfx950 only.  Packed-fp32 instruction selection is switched

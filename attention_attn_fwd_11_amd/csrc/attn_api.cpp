@@ -173,7 +173,7 @@ const char* attn_status_str(attn_status_t s) {
     case ATTN_ERR_SHAPE: return "inconsistent or invalid sizes";
     case ATTN_ERR_UNSUPPORTED: return "unsupported head dimension or dtype";
     case ATTN_ERR_ALIGN: return "pointer not 16-byte aligned";
-    case ATTN_ERR_WORKSPACE: return "decode workspace missing or too small";
+    case ATTN_ERR_WORKSPACE: return "workspace missing or too small";
     case ATTN_ERR_HIP: return "HIP runtime error";
     case ATTN_ERR_VALUE: return "non-finite scale";
   }
@@ -181,6 +181,11 @@ const char* attn_status_str(attn_status_t s) {
 }
 
 const char* attn_last_hip_error(void) { return g_hip_error; }
+
+size_t attn_prefill_rope_workspace_bytes(int32_t B, int32_t H_kv, int32_t S_kv, int32_t d) {
+  if (B < 0 || H_kv < 0 || S_kv < 0 || d < 0) return 0;
+  return (size_t)B * H_kv * S_kv * d * 2;
+}
 
 size_t attn_decode_workspace_bytes(int32_t B, int32_t H_q, int32_t H_kv, int32_t S_kv, int32_t d) {
   return workspace_bytes(B, H_q, H_kv, S_kv, d);
@@ -213,8 +218,8 @@ attn_status_t attn_prefill_fwd(const void* q, const void* k, const void* v, void
 attn_status_t attn_prefill_rope_fwd(const void* q, const void* k, const void* v, void* o, int32_t B,
                                     int32_t H_q, int32_t H_kv, int32_t S_q, int32_t S_kv, int32_t d,
                                     int32_t causal, float scale, const int32_t* kv_lens,
-                                    const float* rope_table, int32_t rope_rows, attn_dtype_t dtype,
-                                    void* stream) {
+                                    const float* rope_table, int32_t rope_rows, void* workspace,
+                                    size_t workspace_bytes, attn_dtype_t dtype, void* stream) {
   g_hip_error[0] = '\0';
   attn_status_t st = check_common(q, k, v, o, B, H_q, H_kv, S_q, S_kv, d, causal, scale, dtype);
   if (st != ATTN_OK) return st;
@@ -223,6 +228,10 @@ attn_status_t attn_prefill_rope_fwd(const void* q, const void* k, const void* v,
   if (rope_rows < S_kv || rope_rows < 1) return ATTN_ERR_SHAPE;   // every key position has a row
   if ((int64_t)B * S_q > 0 && S_kv > 0 && !rope_table) return ATTN_ERR_NULL;
   if (rope_table && !aligned16(rope_table)) return ATTN_ERR_ALIGN;
+  if (workspace) {
+    if (workspace_bytes < attn_prefill_rope_workspace_bytes(B, H_kv, S_kv, d)) return ATTN_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return ATTN_ERR_ALIGN;
+  }
   if ((int64_t)B * S_q == 0) return ATTN_OK;  // nothing to compute
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (S_kv == 0) {
@@ -234,6 +243,12 @@ attn_status_t attn_prefill_rope_fwd(const void* q, const void* k, const void* v,
   p.B = B; p.Hq = H_q; p.Hkv = H_kv; p.Sq = S_q; p.Skv = S_kv; p.d = d; p.causal = causal;
   p.scale_log2 = (float)((double)scale * 1.4426950408889634);
   p.rope = rope_table; p.rope_rows = rope_rows;
+  p.rope_k = workspace ? 0 : 1;
+  if (workspace) {   // keys rotated once into the workspace, Q in the kernel
+    hipError_t e = attn::launch_rope_rows(k, workspace, rope_table, kv_lens, B, H_kv, S_kv, d, s);
+    if (e != hipSuccess) return hip_fail("rope launch", e);
+    p.k = workspace;
+  }
   hipError_t e = attn::launch_prefill_bf16(p, s);
   return e == hipSuccess ? ATTN_OK : hip_fail("prefill launch", e);
 }

@@ -104,6 +104,24 @@ __device__ __forceinline__ void buffer_to_lds16(__amdgpu_buffer_rsrc_t rsrc, voi
 // global -> LDS copies).
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
+// Rotary embedding of 8 feature pairs: x1 holds bf16 features f .. f+7, x2
+// the partners f+d/2 .. f+d/2+7; c0/c1 and s0/s1 the cos and sin of the 8
+// angles.  (x1, x2) -> (x1 c - x2 s, x2 c + x1 s) in fp32, rounded to bf16.
+__device__ __forceinline__ void rope8(u32x4& x1, u32x4& x2, f32x4 c0, f32x4 c1, f32x4 s0, f32x4 s1) {
+  u32x4 y1, y2;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const float a0 = __builtin_bit_cast(float, x1[w] << 16), a1 = __builtin_bit_cast(float, x1[w] & 0xffff0000u);
+    const float b0 = __builtin_bit_cast(float, x2[w] << 16), b1 = __builtin_bit_cast(float, x2[w] & 0xffff0000u);
+    const float ca = w < 2 ? c0[2 * w] : c1[2 * w - 4], cb = w < 2 ? c0[2 * w + 1] : c1[2 * w - 3];
+    const float sa = w < 2 ? s0[2 * w] : s1[2 * w - 4], sb = w < 2 ? s0[2 * w + 1] : s1[2 * w - 3];
+    y1[w] = pack_bf16x2(fmaf(a0, ca, -b0 * sa), fmaf(a1, cb, -b1 * sb));
+    y2[w] = pack_bf16x2(fmaf(b0, ca, a0 * sa), fmaf(b1, cb, a1 * sb));
+  }
+  x1 = y1;
+  x2 = y2;
+}
+
 // Value of lane l^32 (the other half of the wave), via v_permlane32_swap:
 // a VALU op, so no trip through the LDS crossbar.  swap(x, x) yields
 // {x of lanes 0-31 in both halves, x of lanes 32-63 in both halves}.

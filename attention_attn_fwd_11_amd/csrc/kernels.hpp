@@ -27,8 +27,11 @@ struct PrefillParams {
   // Rotary embedding (rope != nullptr, bf16 only): table [rope_rows, d] fp32,
   // columns f < d/2 the cos and d/2 + f the sin of position p's angle for
   // frequency f; Q and K are rotated (rotate-half pairs) before the scores.
+  // rope_k = 0: k already holds rotated keys (launch_rope_rows), so only Q
+  // is rotated in the kernel.
   const float* rope;
   int rope_rows;
+  int rope_k;
 };
 
 struct DecodeParams {
@@ -62,5 +65,10 @@ hipError_t launch_prefill_f32(const PrefillParams& p, hipStream_t stream);
 hipError_t launch_prefill_bf16(const PrefillParams& p, hipStream_t stream);
 hipError_t launch_decode_bf16(const DecodeParams& p, hipStream_t stream);
 hipError_t launch_zero_fill(void* dst, size_t bytes, hipStream_t stream);
+// Rotary embedding of key rows into dst (same [B, H, S, d] bf16 layout as
+// src): row j of every head at position j; rows j >= kv_lens[b] (when given)
+// are skipped.
+hipError_t launch_rope_rows(const void* src, void* dst, const float* table, const int32_t* kv_lens,
+                            int B, int H, int S, int d, hipStream_t stream);
 
 }  // namespace attn

@@ -106,31 +106,14 @@ struct Tile {
   }
 };
 
-// Rotary embedding of 8 feature pairs: x1 holds bf16 features f .. f+7, x2
-// the partners f+d/2 .. f+d/2+7; c0/c1 and s0/s1 the cos and sin of the 8
-// angles.  (x1, x2) -> (x1 c - x2 s, x2 c + x1 s) in fp32, rounded to bf16.
-__device__ __forceinline__ void rope8(u32x4& x1, u32x4& x2, f32x4 c0, f32x4 c1, f32x4 s0, f32x4 s1) {
-  u32x4 y1, y2;
-#pragma unroll
-  for (int w = 0; w < 4; ++w) {
-    const float a0 = __builtin_bit_cast(float, x1[w] << 16), a1 = __builtin_bit_cast(float, x1[w] & 0xffff0000u);
-    const float b0 = __builtin_bit_cast(float, x2[w] << 16), b1 = __builtin_bit_cast(float, x2[w] & 0xffff0000u);
-    const float ca = w < 2 ? c0[2 * w] : c1[2 * w - 4], cb = w < 2 ? c0[2 * w + 1] : c1[2 * w - 3];
-    const float sa = w < 2 ? s0[2 * w] : s1[2 * w - 4], sb = w < 2 ? s0[2 * w + 1] : s1[2 * w - 3];
-    y1[w] = pack_bf16x2(fmaf(a0, ca, -b0 * sa), fmaf(a1, cb, -b1 * sb));
-    y2[w] = pack_bf16x2(fmaf(b0, ca, a0 * sa), fmaf(b1, cb, a1 * sb));
-  }
-  x1 = y1;
-  x2 = y2;
-}
-
 // POS: the scale is >= 0, so the block extreme of the raw scores is their
 // max (a negative scale needs their min).  Causal d = 64 is held to 128
 // registers so two workgroups share a CU (four waves per SIMD; its LDS
 // stages take 64 KiB); the other variants run one workgroup per CU.  ROPE:
-// Q and K are rotated by the rotary table before the scores.
-template <int D, bool CAUSAL, bool POS, bool ROPE>
-__global__ __launch_bounds__(Cfg<D>::kThreads, (D == 64 && CAUSAL && !ROPE) ? 4 : 1) void prefill_bf16_kernel(PrefillParams p) {
+// 0 none; 1 Q rows are rotated by the rotary table as they are loaded (K
+// arrives rotated); 2 Q and every K stage are rotated.
+template <int D, bool CAUSAL, bool POS, int ROPE>
+__global__ __launch_bounds__(Cfg<D>::kThreads, (D == 64 && CAUSAL && ROPE < 2) ? 4 : 1) void prefill_bf16_kernel(PrefillParams p) {
   using T = Tile<D>;
   constexpr int kThreads = Cfg<D>::kThreads;
   constexpr int kRows = Cfg<D>::kRows;
@@ -237,7 +220,7 @@ __global__ __launch_bounds__(Cfg<D>::kThreads, (D == 64 && CAUSAL && !ROPE) ? 4 
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
       qreg[ks] = as_bf16x8(ld16(qp + (int64_t)r * qs + 16 * ks + 8 * half));
-    if constexpr (ROPE) {
+    if constexpr (ROPE >= 1) {
       // this row's position (bottom-right aligned; rows that see no key use 0)
       const int pos = min(max(r + n - sq, 0), p.rope_rows - 1);
       const float* cs = p.rope + (int64_t)pos * D;
@@ -331,11 +314,15 @@ __global__ __launch_bounds__(Cfg<D>::kThreads, (D == 64 && CAUSAL && !ROPE) ? 4 
   // fetched into registers when the stage's copies are issued and applied
   // after the stage has landed.
   constexpr int HS = T::kSlots / 2;
-  constexpr int RIT = ROPE ? kStage * HS / kThreads : 1;   // items per thread per stage
-  f32x4 rcs[RIT][4];
+  constexpr int RIT = ROPE == 2 ? kStage * HS / kThreads : 1;   // items per thread per stage
+  // d = 256 has no registers to hold the table rows across a block: they are
+  // fetched after the stage has landed, two items at a time, just before
+  // their rotation (rope_late).
+  constexpr bool kLateFetch = D == 256;
+  f32x4 rcs[kLateFetch ? 1 : RIT][4];
   auto rope_fetch = [&](int j0) {
 #pragma unroll
-    for (int i = 0; i < RIT; ++i) {
+    for (int i = 0; i < (kLateFetch ? 0 : RIT); ++i) {
       const int it = tid + i * kThreads, r = it / HS, sl = it % HS;
       const float* c = p.rope + (int64_t)min(j0 + r, p.rope_rows - 1) * D + 8 * sl;
       rcs[i][0] = *reinterpret_cast<const f32x4*>(c);
@@ -347,7 +334,7 @@ __global__ __launch_bounds__(Cfg<D>::kThreads, (D == 64 && CAUSAL && !ROPE) ? 4 
   auto rope_apply = [&](auto stage_c) {
     unsigned char* kb = kbuf(stage_c);
 #pragma unroll
-    for (int i = 0; i < RIT; ++i) {
+    for (int i = 0; i < (kLateFetch ? 0 : RIT); ++i) {
       const int it = tid + i * kThreads, r = it / HS, sl = it % HS;
       u32x4* a = reinterpret_cast<u32x4*>(kb + T::off(r, sl));
       u32x4* b = reinterpret_cast<u32x4*>(kb + T::off(r, sl + HS));
@@ -355,6 +342,22 @@ __global__ __launch_bounds__(Cfg<D>::kThreads, (D == 64 && CAUSAL && !ROPE) ? 4 
       rope8(x1, x2, rcs[i][0], rcs[i][1], rcs[i][2], rcs[i][3]);
       *a = x1;
       *b = x2;
+    }
+  };
+  auto rope_late = [&](auto stage_c, int j0) {
+    unsigned char* kb = kbuf(stage_c);
+#pragma unroll
+    for (int i = 0; i < RIT; ++i) {
+      const int it = tid + i * kThreads, r = it / HS, sl = it % HS;
+      const float* c = p.rope + (int64_t)min(j0 + r, p.rope_rows - 1) * D + 8 * sl;
+      u32x4* a = reinterpret_cast<u32x4*>(kb + T::off(r, sl));
+      u32x4* b = reinterpret_cast<u32x4*>(kb + T::off(r, sl + HS));
+      u32x4 x1 = *a, x2 = *b;
+      rope8(x1, x2, *reinterpret_cast<const f32x4*>(c), *reinterpret_cast<const f32x4*>(c + 4),
+            *reinterpret_cast<const f32x4*>(c + D / 2), *reinterpret_cast<const f32x4*>(c + D / 2 + 4));
+      *a = x1;
+      *b = x2;
+      if (i % 2 == 1) __builtin_amdgcn_sched_barrier(0);   // at most two items' table rows live
     }
   };
 
@@ -501,7 +504,7 @@ __global__ __launch_bounds__(Cfg<D>::kThreads, (D == 64 && CAUSAL && !ROPE) ? 4 
       if (more) {
         load_k(Sn{}, (sb + 1) * kStage);
         load_v(Sn{}, (sb + 1) * kStage);
-        if constexpr (ROPE) rope_fetch((sb + 1) * kStage);
+        if constexpr (ROPE == 2 && !kLateFetch) rope_fetch((sb + 1) * kStage);
       }
       block(st_c, std::integral_constant<int, 0>{}, sb);
     } else {
@@ -510,16 +513,16 @@ __global__ __launch_bounds__(Cfg<D>::kThreads, (D == 64 && CAUSAL && !ROPE) ? 4 
       if (more) {
         load_k(Sn{}, (sb + 1) * kStage);
         load_v(Sn{}, (sb + 1) * kStage);
-        if constexpr (ROPE) rope_fetch((sb + 1) * kStage);
+        if constexpr (ROPE == 2 && !kLateFetch) rope_fetch((sb + 1) * kStage);
       }
       if (2 * sb + 1 < n_blocks) block(st_c, std::integral_constant<int, 1>{}, 2 * sb + 1);
     }
     __builtin_amdgcn_sched_barrier(0);
     wait_vmem();
     __syncthreads();
-    if constexpr (ROPE) {
+    if constexpr (ROPE == 2) {
       if (more) {             // the next stage has landed: rotate its keys
-        rope_apply(Sn{});
+        if constexpr (kLateFetch) rope_late(Sn{}, (sb + 1) * kStage); else rope_apply(Sn{});
         __syncthreads();
       }
     }
@@ -527,13 +530,14 @@ __global__ __launch_bounds__(Cfg<D>::kThreads, (D == 64 && CAUSAL && !ROPE) ? 4 
   if (n_stages > 0) {
     load_k(std::integral_constant<int, 0>{}, 0);
     load_v(std::integral_constant<int, 0>{}, 0);
-    if constexpr (ROPE) rope_fetch(0);
+    if constexpr (ROPE == 2 && !kLateFetch) rope_fetch(0);
   }
   wait_vmem();
   __syncthreads();
-  if constexpr (ROPE) {
+  if constexpr (ROPE == 2) {
     if (n_stages > 0) {
-      rope_apply(std::integral_constant<int, 0>{});
+      if constexpr (kLateFetch) rope_late(std::integral_constant<int, 0>{}, 0);
+      else rope_apply(std::integral_constant<int, 0>{});
       __syncthreads();
     }
   }
@@ -569,12 +573,15 @@ hipError_t launch(const PrefillParams& p, hipStream_t stream) {
   dim3 grid((unsigned)n_pr * p.Hq * p.B);
   const dim3 block(Cfg<D>::kThreads);
   const bool pos = p.scale_log2 >= 0.f;
-  if (p.rope) {
-    if (pos) hipLaunchKernelGGL((prefill_bf16_kernel<D, CAUSAL, true, true>), grid, block, 0, stream, p);
-    else hipLaunchKernelGGL((prefill_bf16_kernel<D, CAUSAL, false, true>), grid, block, 0, stream, p);
+  if (p.rope && p.rope_k) {
+    if (pos) hipLaunchKernelGGL((prefill_bf16_kernel<D, CAUSAL, true, 2>), grid, block, 0, stream, p);
+    else hipLaunchKernelGGL((prefill_bf16_kernel<D, CAUSAL, false, 2>), grid, block, 0, stream, p);
+  } else if (p.rope) {
+    if (pos) hipLaunchKernelGGL((prefill_bf16_kernel<D, CAUSAL, true, 1>), grid, block, 0, stream, p);
+    else hipLaunchKernelGGL((prefill_bf16_kernel<D, CAUSAL, false, 1>), grid, block, 0, stream, p);
   } else {
-    if (pos) hipLaunchKernelGGL((prefill_bf16_kernel<D, CAUSAL, true, false>), grid, block, 0, stream, p);
-    else hipLaunchKernelGGL((prefill_bf16_kernel<D, CAUSAL, false, false>), grid, block, 0, stream, p);
+    if (pos) hipLaunchKernelGGL((prefill_bf16_kernel<D, CAUSAL, true, 0>), grid, block, 0, stream, p);
+    else hipLaunchKernelGGL((prefill_bf16_kernel<D, CAUSAL, false, 0>), grid, block, 0, stream, p);
   }
   return hipGetLastError();
 }

@@ -56,7 +56,7 @@ typedef enum {
     ATTN_ERR_SHAPE = 2,       /* inconsistent or negative sizes                  */
     ATTN_ERR_UNSUPPORTED = 3, /* valid but not implemented: d, dtype             */
     ATTN_ERR_ALIGN = 4,       /* a pointer is not 16-byte aligned                */
-    ATTN_ERR_WORKSPACE = 5,   /* decode workspace missing or too small           */
+    ATTN_ERR_WORKSPACE = 5,   /* a workspace missing or too small                */
     ATTN_ERR_HIP = 6,         /* a HIP runtime call or kernel launch failed      */
     ATTN_ERR_VALUE = 7        /* non-finite scale                                */
 } attn_status_t;
@@ -103,16 +103,31 @@ attn_status_t attn_prefill_fwd(const void* q, const void* k, const void* v, void
  * in fp32, rounded to bf16, before the scores.  Key j is at position j;
  * query i of a sequence with n keys at n - S_q + i (the causal mask's
  * bottom-right alignment; rows that see no key use position 0).  V is not
- * rotated.  RoPE is the step "GPU learning day 24: Operator Fusion",
- * section 6 (exercise 1's reference answer), places inside the attention
- * kernel; the pages give no formula, and this is the rotate-half form.
- * Keys are rotated once per workgroup in LDS as each K stage arrives.
+ * rotated.  "GPU learning day 24: Operator Fusion", section 6 (exercise 1's
+ * reference answer), puts RoPE either in the QKV projection's epilogue or
+ * inside the attention kernel; it gives no formula, and this is the
+ * rotate-half form.  Q is always rotated inside the kernel, as its rows
+ * are loaded.  K:
+ *   workspace == NULL: each K stage is rotated in LDS inside the kernel
+ *     (no extra memory; the work repeats for every query tile).
+ *   workspace != NULL: device buffer of at least
+ *     attn_prefill_rope_workspace_bytes(B, H_kv, S_kv, d) bytes (else
+ *     ATTN_ERR_WORKSPACE), 16-byte aligned (else ATTN_ERR_ALIGN), owned by
+ *     the caller and not read before the call: a first kernel writes the
+ *     rotated keys there once (in place of the projection's epilogue) and
+ *     the attention kernel reads them.  Rows past kv_lens[b] are left as
+ *     they were.
+ * Both give bit-identical O (the rotation is the same fp32 arithmetic).
  */
 attn_status_t attn_prefill_rope_fwd(const void* q, const void* k, const void* v, void* o, int32_t B,
                                     int32_t H_q, int32_t H_kv, int32_t S_q, int32_t S_kv, int32_t d,
                                     int32_t causal, float scale, const int32_t* kv_lens,
-                                    const float* rope_table, int32_t rope_rows, attn_dtype_t dtype,
-                                    void* stream);
+                                    const float* rope_table, int32_t rope_rows, void* workspace,
+                                    size_t workspace_bytes, attn_dtype_t dtype, void* stream);
+
+/* Bytes of the key workspace attn_prefill_rope_fwd takes: B*H_kv*S_kv*d*2
+ * (0 for a negative argument). */
+size_t attn_prefill_rope_workspace_bytes(int32_t B, int32_t H_kv, int32_t S_kv, int32_t d);
 
 /*
  * Attention forward over packed variable-length sequences (bf16).

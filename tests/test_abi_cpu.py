@@ -33,7 +33,8 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
-    assert {"attn_prefill_fwd", "attn_prefill_rope_fwd", "attn_prefill_varlen_fwd", "attn_decode_fwd",
+    assert {"attn_prefill_fwd", "attn_prefill_rope_fwd", "attn_prefill_rope_workspace_bytes",
+            "attn_prefill_varlen_fwd", "attn_decode_fwd",
             "attn_decode_paged_fwd",
             "attn_decode_workspace_bytes", "attn_status_str", "attn_last_hip_error"} <= set(names)
     for n in names:
@@ -93,9 +94,9 @@ def test_decode_rejects(lib, kw, code):
 
 
 def prefill_rope(q=P, k=P, v=P, o=P, B=1, Hq=2, Hkv=2, Sq=8, Skv=8, d=64, causal=1, scale=0.125,
-                 lens=NULL, table=P, rows=8, dtype=attn.ATTN_BF16):
+                 lens=NULL, table=P, rows=8, ws=NULL, ws_bytes=0, dtype=attn.ATTN_BF16):
     return attn.attn_prefill_rope_fwd(q, k, v, o, B, Hq, Hkv, Sq, Skv, d, causal, scale, lens, table,
-                                      rows, dtype, NULL)
+                                      rows, ws, ws_bytes, dtype, NULL)
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -104,9 +105,16 @@ def prefill_rope(q=P, k=P, v=P, o=P, B=1, Hq=2, Hkv=2, Sq=8, Skv=8, d=64, causal
     (dict(dtype=attn.ATTN_F32), 3), (dict(d=96), 3),
     (dict(table=MIS), 4), (dict(q=MIS), 4),
     (dict(scale=math.nan), 7),
+    (dict(ws=P, ws_bytes=1 * 2 * 8 * 64 * 2 - 1), 5), (dict(ws=MIS, ws_bytes=4096), 4),
 ])
 def test_prefill_rope_rejects(lib, kw, code):
     assert prefill_rope(**kw) == code
+
+
+def test_prefill_rope_workspace_bytes(lib):
+    assert attn.attn_prefill_rope_workspace_bytes(2, 8, 4096, 128) == 2 * 8 * 4096 * 128 * 2
+    assert attn.attn_prefill_rope_workspace_bytes(1, 1, 0, 64) == 0
+    assert attn.attn_prefill_rope_workspace_bytes(-1, 1, 1, 64) == 0
 
 
 def prefill_varlen(q=P, k=P, v=P, o=P, cq=P, ck=P, B=2, Hq=4, Hkv=2, mq=64, mk=64, tq=100, tk=100, d=64,

@@ -1,8 +1,11 @@
-"""Prefill with the rotary embedding fused in (attn_prefill_rope_fwd) against
-the fp64 oracle that rotates Q and K first (oracle.rope), plus two
-properties: an identity table (cos 1, sin 0) gives exactly the plain
-prefill's output, and a table of random rotations applied to Q and K on the
-host before a plain prefill gives the same scores up to bf16 rounding."""
+"""Prefill with the rotary embedding (attn_prefill_rope_fwd), with K rotated
+inside the attention kernel or once by a pre-pass into a workspace, against
+the fp64 oracle that rotates Q and K first (oracle.rope).  Properties: both
+K placements give identical bits; an identity table (cos 1, sin 0) gives
+exactly the plain prefill's output; rotating Q and K on the host before a
+plain prefill agrees to bf16 rounding; the pre-pass's rotated keys match
+the oracle's rotation to one bf16 rounding and leave rows past kv_lens
+alone."""
 import sys
 
 import numpy as np
@@ -18,6 +21,11 @@ from tests.gpu_util import assert_close, convex_bound_ok, sample_rows
 pytestmark = pytest.mark.gpu
 
 DEV = "cuda:0"
+
+
+def workspace(B, Hkv, S, d):
+    n = attn.attn_prefill_rope_workspace_bytes(B, Hkv, S, d)
+    return torch.empty(max(n, 16), dtype=torch.uint8, device=DEV)
 
 
 def say(msg):
@@ -38,9 +46,13 @@ CASES = [
 ]
 
 
-@pytest.mark.parametrize("case", CASES, ids=lambda c: f"B{c[0]}H{c[1]}-{c[2]}-q{c[3]}k{c[4]}-d{c[5]}"
-                                                    f"-c{int(c[6])}-l{int(c[7] is not None)}")
+CASE_IDS = [f"B{c[0]}H{c[1]}-{c[2]}-q{c[3]}k{c[4]}-d{c[5]}-c{int(c[6])}-l{int(c[7] is not None)}"
+            for c in CASES]
+
+
+@pytest.mark.parametrize("case", CASES, ids=CASE_IDS)
 def test_rope_prefill_matches_oracle(case):
+    """Both K placements against the oracle, and bit for bit against each other."""
     B, Hq, Hkv, Sq, Skv, d, causal, lens, spare = case
     say(f"rope prefill {case}")
     x = wl.random_problem(B, Hq, Hkv, Sq, Skv, d, dtype="bf16", device=DEV, seed=41)
@@ -48,10 +60,42 @@ def test_rope_prefill_matches_oracle(case):
     scale = 1.0 / np.sqrt(d)
     lens_t = None if lens is None else torch.tensor(lens, dtype=torch.int32, device=DEV)
     o = attn.prefill(x["q"], x["k"], x["v"], causal=causal, scale=scale, kv_lens=lens_t, rope=table)
+    o2 = attn.prefill(x["q"], x["k"], x["v"], causal=causal, scale=scale, kv_lens=lens_t, rope=table,
+                      rope_workspace=workspace(B, Hkv, Skv, d))
     torch.cuda.synchronize()
     ref = orope.attention_rope(x["q"].cpu(), x["k"].cpu(), x["v"].cpu(), causal, scale, table.cpu(),
                                kv_lens=lens)
     assert_close(o, ref, torch.bfloat16, f"rope prefill {case}")
+    assert torch.equal(o, o2), "K rotated in the kernel and by the pre-pass must give the same bits"
+
+
+@pytest.mark.parametrize("d", [64, 128, 256])
+def test_rope_prepass_keys(d):
+    """The workspace holds rope(K) (the oracle's fp64 rotation, one bf16
+    rounding apart) for rows below kv_lens and is untouched past them."""
+    say(f"rope pre-pass keys d{d}")
+    B, Hkv, S = 3, 2, 300
+    x = wl.random_problem(B, Hkv, Hkv, 4, S, d, dtype="bf16", device=DEV, seed=44)
+    table = wl.rope_table(S + 9, d, theta=300.0, device=DEV)
+    lens = [300, 17, 0]
+    ws = workspace(B, Hkv, S, d)
+    ws.fill_(0x7f)                                  # bf16 0x7f7f: a large finite sentinel
+    attn.prefill(x["q"], x["k"], x["v"], causal=True, kv_lens=torch.tensor(lens, dtype=torch.int32,
+                 device=DEV), rope=table, rope_workspace=ws)
+    torch.cuda.synchronize()
+    kr = ws[: B * Hkv * S * d * 2].view(torch.bfloat16).view(B, Hkv, S, d).cpu()
+    ref = orope.rope(x["k"].cpu(), table.cpu(), np.arange(S))
+    sentinel = torch.tensor([0x7f7f], dtype=torch.int16).view(torch.bfloat16)[0]
+    for b, n in enumerate(lens):
+        got = kr[b, :, :n].double().numpy()
+        want = ref[b, :, :n]
+        # fp32 products and an fma (error ~2^-23 of |x1| + |x2|, which matters
+        # only where the two terms cancel), then one rounding to bf16 (half
+        # an ulp, at most 2^-8 of the value)
+        mag = float(np.abs(x["k"][b].float().cpu().numpy()).max())
+        tol = 2.0 ** -8 * np.abs(want) + 2.0 ** -20 * mag
+        assert np.all(np.abs(got - want) <= tol), f"batch {b}: {np.abs(got - want).max():.3g}"
+        assert bool((kr[b, :, n:] == sentinel).all()), f"batch {b}: rows past kv_lens written"
 
 
 @pytest.mark.parametrize("d", [64, 128, 256])
@@ -61,9 +105,12 @@ def test_identity_table_equals_plain_prefill(d):
     x = wl.random_problem(B, Hq, Hkv, S, S, d, dtype="bf16", device=DEV, seed=42)
     table = torch.cat([torch.ones(S, d // 2), torch.zeros(S, d // 2)], dim=1).to(DEV)
     a = attn.prefill(x["q"], x["k"], x["v"], causal=True, rope=table)
+    a2 = attn.prefill(x["q"], x["k"], x["v"], causal=True, rope=table,
+                      rope_workspace=workspace(B, Hkv, S, d))
     b = attn.prefill(x["q"], x["k"], x["v"], causal=True)
     torch.cuda.synchronize()
     assert torch.equal(a, b), "cos 1 / sin 0 must leave Q and K unchanged"
+    assert torch.equal(a2, b), "cos 1 / sin 0 must leave Q and K unchanged (pre-pass)"
 
 
 def test_rope_equals_host_rotation_then_plain_prefill():
@@ -93,7 +140,10 @@ def test_rope_workload_sampled():
     x = wl.generate(w, DEV)
     table = wl.rope_table(w.Skv, w.d, device=DEV)
     o = attn.prefill(x["q"], x["k"], x["v"], causal=True, scale=w.scale, rope=table)
+    o2 = attn.prefill(x["q"], x["k"], x["v"], causal=True, scale=w.scale, rope=table,
+                      rope_workspace=workspace(w.B, w.Hkv, w.Skv, w.d))
     torch.cuda.synchronize()
+    assert torch.equal(o, o2), "K placements differ at the full size"
     ok, finite = convex_bound_ok(o, x["v"], w.Hq)
     assert finite and ok, "output outside the convex hull of V"
     S = w.Sq
