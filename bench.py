@@ -13,9 +13,12 @@ Printed: one JSON line.  `value` is prefill TFLOP/s (algorithmic FLOPs: 4*d
 per visible query/key pair) over the prefill kernel's average event time;
 decode KV-read GB/s (algorithmic K+V bytes, every visible row once) is given
 beside it, with a roofline object for each against MI355X's published peaks
-(dense bf16 MFMA 2516.6 TFLOP/s, HBM 8 TB/s).  The remaining workloads
-(GQA ragged decode, long GQA prefill) are timed the same way and reported
-under "other_workloads".  The CPU oracle is timed on a bounded sample of the
+(dense bf16 MFMA 2516.6 TFLOP/s, HBM 8 TB/s), and the median/min/max of the
+per-call times.  The remaining workloads (GQA ragged decode, long GQA
+prefill, d = 64 and 256, chunked and packed varlen prefill, paged decode,
+RoPE prefill in both key placements, a graph-captured small decode, the
+fp32 parity-sized prefill) are timed the same way and reported under
+"other_workloads".  The CPU oracle is timed on a bounded sample of the
 prefill workload as "cpu_baseline".
 """
 import argparse
@@ -102,6 +105,14 @@ class Timer:
     def mean_ms(self):
         ts = [a.elapsed_time(b) for a, b in self.pairs]
         return sum(ts) / len(ts), ts
+
+
+def spread(ts):
+    """Median, min and max of per-call times (ms)."""
+    s = sorted(ts)
+    n = len(s)
+    med = s[n // 2] if n % 2 else 0.5 * (s[n // 2 - 1] + s[n // 2])
+    return {"median_ms": round(med, 4), "min_ms": round(s[0], 4), "max_ms": round(s[-1], 4)}
 
 
 def cpu_baseline(w, x, seconds):
@@ -222,6 +233,25 @@ def rope_prefill(torch, attn, wl, x, w, steps, warmup):
     return {"shape": w.describe() + " + RoPE", "algorithmic_flop": wl.prefill_flops(w),
             "note": "k_prepass: keys rotated once into a workspace, then Q rotated in the attention "
                     "kernel (ms covers both launches)", **res}
+
+
+def f32_small(torch, attn, wl, dev, steps, warmup):
+    """The fp32 causal prefill B1 H2 S128 d64 (parity-sized; latency-bound, so
+    its time is reported without a roofline fraction)."""
+    w = wl.BY_NAME["prefill_f32_small"]
+    x = wl.generate(w, dev)
+    out = torch.empty_like(x["q"])
+    f = lambda: attn.prefill(x["q"], x["k"], x["v"], causal=True, scale=w.scale, out=out)
+    for _ in range(warmup):
+        f()
+    torch.cuda.synchronize()
+    tm = Timer(torch)
+    for _ in range(steps):
+        tm(f)
+    torch.cuda.synchronize()
+    ms, ts = tm.mean_ms()
+    return {"shape": w.describe(), "ms": round(ms, 4), **spread(ts),
+            "algorithmic_flop": wl.prefill_flops(w)}
 
 
 def paged_decode(torch, attn, wl, x, w, steps, warmup, page_size=128):
@@ -381,8 +411,8 @@ def main():
         td(fd)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    ms_p, _ = tp.mean_ms()
-    ms_d, _ = td.mean_ms()
+    ms_p, ts_p = tp.mean_ms()
+    ms_d, ts_d = td.mean_ms()
 
     flops_p = wl.prefill_flops(wp)
     bytes_d = wl.decode_kv_bytes(wd, inputs[wd.name]["kv_lens"].cpu())
@@ -442,6 +472,7 @@ def main():
             "workload": "causal prefill bf16 B4 H32 S4096 d128 + decode bf16 B64 H32 L4096 d128",
             "prefill": wp.describe(), "decode": wd.describe(),
             "prefill_ms": round(ms_p, 4), "decode_ms": round(ms_d, 4),
+            "prefill_spread": spread(ts_p), "decode_spread": spread(ts_d),
         },
         "prefill_tflops": round(tflops, 2),
         "prefill_frac_of_mfma_peak": round(tflops / PEAK_BF16_TFLOPS, 4),
@@ -459,6 +490,7 @@ def main():
         other["prefill_rope_bf16_b4h32s4096"] = rope_prefill(torch, attn, wl, inputs[wp.name], wp,
                                                              args.steps, args.warmup)
     other["decode_graph_small"] = decode_graph(torch, attn, wl, dev)
+    other["prefill_f32_small"] = f32_small(torch, attn, wl, dev, args.steps, args.warmup)
     probe = read_probe(torch, dev)
     out["context"] = {
         "read_probe": probe,
