@@ -49,6 +49,15 @@ attn_status_t check_common(const void* q, const void* k, const void* v, const vo
   return ATTN_OK;
 }
 
+// Causal prefill: pair query tiles n_qt-1-p and p in one workgroup when the
+// queries span at least half of the keys (the tiles' work then grows along
+// the diagonal and the pairs even it out); a short chunk of queries at the
+// end of a long cache has tiles of nearly equal work, where pairing would
+// only halve the number of workgroups.
+int pair_tiles(int32_t causal, int32_t S_q, int32_t S_kv) {
+  return causal && 2LL * S_q >= S_kv ? 1 : 0;
+}
+
 // Decode work decomposition.  Query groups (G >= 2) with at most
 // kDecodeMaxBatch sequences use the balanced pass: fixed units of
 // kDecodeUnit keys spread evenly over a persistent grid.  Otherwise the cache
@@ -210,6 +219,7 @@ attn_status_t attn_prefill_fwd(const void* q, const void* k, const void* v, void
   attn::PrefillParams p{};
   p.q = q; p.k = k; p.v = v; p.o = o; p.kv_lens = kv_lens;
   p.B = B; p.Hq = H_q; p.Hkv = H_kv; p.Sq = S_q; p.Skv = S_kv; p.d = d; p.causal = causal;
+  p.pair = pair_tiles(causal, S_q, S_kv);
   p.scale_log2 = (float)((double)scale * 1.4426950408889634);
   hipError_t e = dtype == ATTN_F32 ? attn::launch_prefill_f32(p, s) : attn::launch_prefill_bf16(p, s);
   return e == hipSuccess ? ATTN_OK : hip_fail("prefill launch", e);
@@ -241,6 +251,7 @@ attn_status_t attn_prefill_rope_fwd(const void* q, const void* k, const void* v,
   attn::PrefillParams p{};
   p.q = q; p.k = k; p.v = v; p.o = o; p.kv_lens = kv_lens;
   p.B = B; p.Hq = H_q; p.Hkv = H_kv; p.Sq = S_q; p.Skv = S_kv; p.d = d; p.causal = causal;
+  p.pair = pair_tiles(causal, S_q, S_kv);
   p.scale_log2 = (float)((double)scale * 1.4426950408889634);
   p.rope = rope_table; p.rope_rows = rope_rows;
   p.rope_k = workspace ? 0 : 1;
@@ -291,6 +302,7 @@ attn_status_t attn_prefill_varlen_fwd(const void* q, const void* k, const void* 
   p.q = q; p.k = k; p.v = v; p.o = o; p.kv_lens = nullptr;
   p.B = B; p.Hq = H_q; p.Hkv = H_kv; p.Sq = max_seqlen_q; p.Skv = max_seqlen_k; p.d = d;
   p.causal = causal;
+  p.pair = pair_tiles(causal, max_seqlen_q, max_seqlen_k);
   p.scale_log2 = (float)((double)scale * 1.4426950408889634);
   p.cu_q = cu_seqlens_q; p.cu_k = cu_seqlens_k; p.total_q = total_q; p.total_k = total_k;
   hipError_t e = attn::launch_prefill_bf16(p, s);

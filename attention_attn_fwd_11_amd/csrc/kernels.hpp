@@ -32,6 +32,11 @@ struct PrefillParams {
   const float* rope;
   int rope_rows;
   int rope_k;
+  // Causal only: 1 = one workgroup takes query tiles n_qt-1-p and p (equal
+  // work per workgroup when queries and keys span the same positions); 0 =
+  // one tile per workgroup, heaviest first (a chunk of queries at the end of
+  // a long cache, where every tile has about the same work).
+  int pair;
 };
 
 struct DecodeParams {

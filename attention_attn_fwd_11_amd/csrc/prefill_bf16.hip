@@ -143,9 +143,11 @@ __global__ __launch_bounds__(Cfg<D>::kThreads, (D == 64 && CAUSAL && ROPE < 2) ?
   const int n_qt = (p.Sq + kRows - 1) / kRows;
   const int G = p.Hq / p.Hkv;
   const int id = blockIdx.x;
-  // Causal: workgroup pair index pr covers tiles n_qt-1-pr then pr (one
-  // tile when they coincide); non-causal: one tile, pr.
-  const int n_pr = CAUSAL ? (n_qt + 1) / 2 : n_qt;
+  // Causal and paired: workgroup pair index pr covers tiles n_qt-1-pr then
+  // pr (one tile when they coincide); causal unpaired: tile n_qt-1-pr
+  // (heaviest first); non-causal: tile pr.
+  const bool pair = CAUSAL && p.pair != 0;
+  const int n_pr = pair ? (n_qt + 1) / 2 : n_qt;
   int pr, h, b;
   if ((p.B * p.Hkv) % kXcds == 0) {
     const int xcd = id % kXcds, slot = id / kXcds;
@@ -197,12 +199,12 @@ __global__ __launch_bounds__(Cfg<D>::kThreads, (D == 64 && CAUSAL && ROPE < 2) ?
   const int kv_row_bytes = (int)kvs * 2;
   // this sequence's own tiles (fewer than the grid's when it is shorter)
   const int n_qt_b = (sq + kRows - 1) / kRows;
-  const int n_pr_b = CAUSAL ? (n_qt_b + 1) / 2 : n_qt_b;
+  const int n_pr_b = pair ? (n_qt_b + 1) / 2 : n_qt_b;
   if (pr >= n_pr_b) return;         // uniform over the workgroup, before any barrier
 
-  const int n_pass = (CAUSAL && n_qt_b - 1 - pr != pr) ? 2 : 1;
+  const int n_pass = (pair && n_qt_b - 1 - pr != pr) ? 2 : 1;
   for (int pass = 0; pass < n_pass; ++pass) {
-  const int qt = CAUSAL ? (pass == 0 ? n_qt_b - 1 - pr : pr) : pr;
+  const int qt = CAUSAL ? (pass == 0 ? n_qt_b - 1 - pr : pr) : pr;   // unpaired: pass 0 only
   const int tile_row0 = qt * kRows;
   const int wave_row0 = tile_row0 + wave * 32;
   const int my_row = wave_row0 + col;
@@ -569,7 +571,7 @@ __global__ __launch_bounds__(Cfg<D>::kThreads, (D == 64 && CAUSAL && ROPE < 2) ?
 template <int D, bool CAUSAL>
 hipError_t launch(const PrefillParams& p, hipStream_t stream) {
   const int n_qt = (p.Sq + Cfg<D>::kRows - 1) / Cfg<D>::kRows;
-  const int n_pr = CAUSAL ? (n_qt + 1) / 2 : n_qt;
+  const int n_pr = (CAUSAL && p.pair) ? (n_qt + 1) / 2 : n_qt;
   dim3 grid((unsigned)n_pr * p.Hq * p.B);
   const dim3 block(Cfg<D>::kThreads);
   const bool pos = p.scale_log2 >= 0.f;
