@@ -63,6 +63,7 @@ namespace {
 
 constexpr int kKeys = 64;    // keys per compute block
 constexpr int kXcds = 8;                      // accelerator complex dies of an MI355X
+constexpr int kMaxRankB = 256;                // longest-first order up to this many sequences
 constexpr float kRescaleSlack = 8.f;   // base-2 headroom before the accumulator is rescaled
 
 // Workgroup shape per head dimension.  d = 64, 128: 8 waves (two per SIMD),
@@ -161,6 +162,39 @@ __global__ __launch_bounds__(Cfg<D>::kThreads, (D == 64 && CAUSAL && ROPE < 2) ?
     pr = id % n_pr;
     h = (id / n_pr) % p.Hq;
     b = id / (n_pr * p.Hq);
+  }
+  // Longest sequences first: with per-sequence lengths (and at most
+  // kMaxRankB sequences) the batch index decoded above is a rank, and the
+  // workgroup takes the sequence with that many longer ones before it (ties
+  // by index), so the lowest workgroup ids -- dispatched first -- take the
+  // longest sequences.  Every workgroup computes the same order.  The
+  // lengths pass through v_s1, which no copy writes before the first stage.
+  if ((p.kv_lens || p.cu_k) && p.B > 1 && p.B <= kMaxRankB) {
+    int* keys = reinterpret_cast<int*>(v_s1);
+    int* chosen = keys + kMaxRankB;
+    if (tid < p.B) {
+      int len;
+      if (p.cu_k) {
+        const int k0 = min(max(p.cu_k[tid], 0), p.total_k);
+        const int k1 = min(max(p.cu_k[tid + 1], k0), p.total_k);
+        len = min(k1 - k0, p.Skv);
+      } else {
+        len = min(max(p.kv_lens[tid], 0), p.Skv);
+      }
+      keys[tid] = len;
+    }
+    __syncthreads();
+    if (tid < p.B) {
+      const int mine = keys[tid];
+      int rank = 0;
+      for (int j = 0; j < p.B; ++j) {
+        const int o = keys[j];
+        rank += (o > mine || (o == mine && j < tid)) ? 1 : 0;
+      }
+      if (rank == b) *chosen = tid;
+    }
+    __syncthreads();
+    b = *chosen;
   }
   const int g = h / G;
 
