@@ -502,9 +502,11 @@ __global__ __launch_bounds__(Cfg<D>::kThreads, (D == 64 && CAUSAL && ROPE < 2) ?
   };
 
   // Does any row of this wave see a key of block blk?  (wave-uniform; once
-  // false it stays false for later blocks)
+  // false it stays false for later blocks.)  A wave whose rows all lie past
+  // the sequence's end (in a partial last tile) computes nothing; it still
+  // takes part in the copies and barriers.
   auto active = [&](int blk) {
-    return blk < n_blocks && blk * kKeys <= (CAUSAL ? wave_last_row + n - sq : n - 1);
+    return wave_row0 < sq && blk < n_blocks && blk * kKeys <= (CAUSAL ? wave_last_row + n - sq : n - 1);
   };
   auto needs_mask = [&](int blk) {
     const int j0 = blk * kKeys;
