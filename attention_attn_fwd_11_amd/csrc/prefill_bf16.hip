@@ -65,6 +65,8 @@ constexpr int kKeys = 64;    // keys per compute block
 constexpr int kXcds = 8;                      // accelerator complex dies of an MI355X
 constexpr int kMaxRankB = 256;                // longest-first order up to this many sequences
 constexpr float kRescaleSlack = 8.f;   // base-2 headroom before the accumulator is rescaled
+constexpr float kLazyLimit = 256.f;    // 2^kRescaleSlack: the largest P the lazy rescale allows
+static_assert(kLazyLimit == 256.f && kRescaleSlack == 8.f, "kLazyLimit is 2^kRescaleSlack");
 
 // Workgroup shape per head dimension.  d = 64, 128: 8 waves (two per SIMD),
 // 256 query rows, 128-key LDS stages (two compute blocks).  d = 256: the
@@ -458,9 +460,9 @@ __global__ __launch_bounds__(Cfg<D>::kThreads, (D == 64 && CAUSAL && ROPE < 2) ?
     }
   };
 
-  // P = exp2(s*c - m_ref) rounded to bf16 (the B operand of P V); the
-  // running sum is taken from the rounded values (dot2 with (1, 1)).
-  auto probabilities = [&](auto masked_c, const f32x16 (&sacc)[2], u32x4 (&pb)[4]) {
+  // P = exp2(s*c - m_ref) rounded to bf16 (the B operand of P V); returns
+  // this lane's sum of the rounded values (dot2 with (1, 1)).
+  auto probabilities = [&](auto masked_c, const f32x16 (&sacc)[2], u32x4 (&pb)[4]) -> float {
     constexpr bool MASKED = decltype(masked_c)::value;
     const float negm = -mref;
     float psum = 0.f;
@@ -482,7 +484,7 @@ __global__ __launch_bounds__(Cfg<D>::kThreads, (D == 64 && CAUSAL && ROPE < 2) ?
       }
       pb[cc] = u32x4{w[0], w[1], w[2], w[3]};
     }
-    lsum += psum;
+    return psum;
   };
 
   // O^T += V^T P^T from LDS stage S; V^T comes from transpose reads of the
@@ -525,11 +527,21 @@ __global__ __launch_bounds__(Cfg<D>::kThreads, (D == 64 && CAUSAL && ROPE < 2) ?
       u32x4 pb[4];
       scores(st_c, sub_c, sc);
       if (!needs_mask(blk)) {
-        prepare(std::false_type{}, sc, blk * kKeys);
-        probabilities(std::false_type{}, sc, pb);
+        // P against the current reference first: the rescale is due only if
+        // some P exceeds 2^kRescaleSlack, and then this lane's sum of P does
+        // too (or is +inf on a row's first block), so the block extreme is
+        // only computed on that rare path.  The result is the one prepare +
+        // probabilities would give.
+        float psum = probabilities(std::false_type{}, sc, pb);
+        if (__any(!(psum <= kLazyLimit))) {
+          const float m_old = mref;
+          prepare(std::false_type{}, sc, blk * kKeys);
+          if (__any(mref != m_old)) psum = probabilities(std::false_type{}, sc, pb);
+        }
+        lsum += psum;
       } else {
         prepare(std::true_type{}, sc, blk * kKeys);
-        probabilities(std::true_type{}, sc, pb);
+        lsum += probabilities(std::true_type{}, sc, pb);
       }
       __builtin_amdgcn_sched_barrier(0);
       accumulate(st_c, sub_c, pb);
