@@ -245,11 +245,15 @@ __global__ __launch_bounds__(Cfg<D>::kThreads, (D == 64 && CAUSAL && ROPE < 2) ?
   const int wave_row0 = tile_row0 + wave * 32;
   const int my_row = wave_row0 + col;
   const int last_row = min(tile_row0 + kRows, sq) - 1;
+  // diag: row i sees keys j <= i + diag (bottom-right causal: n - sq); d =
+  // 256 runs non-causal calls through this instance with diag = n, which
+  // lets every row see every key.
+  const int diag = (CAUSAL && (D != 256 || p.causal != 0)) ? n - sq : n;
   int kend = n;
-  if (CAUSAL) kend = min(n, max(0, last_row + n - sq + 1));
+  if (CAUSAL) kend = min(n, max(0, last_row + diag + 1));
   const int n_blocks = (kend + kKeys - 1) / kKeys;
   const int wave_last_row = min(wave_row0 + 31, sq - 1);
-  const int my_last = CAUSAL ? my_row + n - sq : n - 1;   // last key this row sees
+  const int my_last = CAUSAL ? my_row + diag : n - 1;   // last key this row sees
 
   // Q^T as the B operand: lane (col, half) holds Q[my_row][16*ks + 8*half .. +7].
   bf16x8 qreg[KS];
@@ -508,11 +512,11 @@ __global__ __launch_bounds__(Cfg<D>::kThreads, (D == 64 && CAUSAL && ROPE < 2) ?
   // the sequence's end (in a partial last tile) computes nothing; it still
   // takes part in the copies and barriers.
   auto active = [&](int blk) {
-    return wave_row0 < sq && blk < n_blocks && blk * kKeys <= (CAUSAL ? wave_last_row + n - sq : n - 1);
+    return wave_row0 < sq && blk < n_blocks && blk * kKeys <= (CAUSAL ? wave_last_row + diag : n - 1);
   };
   auto needs_mask = [&](int blk) {
     const int j0 = blk * kKeys;
-    return (j0 + kKeys > n) || (CAUSAL && j0 + kKeys - 1 > wave_row0 + n - sq);
+    return (j0 + kKeys > n) || (CAUSAL && j0 + kKeys - 1 > wave_row0 + diag);
   };
 
   // ---- the key loop ------------------------------------------------------
@@ -640,7 +644,7 @@ hipError_t launch(const PrefillParams& p, hipStream_t stream) {
 
 hipError_t launch_prefill_bf16(const PrefillParams& p, hipStream_t stream) {
   if (p.d == 64) return p.causal ? launch<64, true>(p, stream) : launch<64, false>(p, stream);
-  if (p.d == 256) return p.causal ? launch<256, true>(p, stream) : launch<256, false>(p, stream);
+  if (p.d == 256) return launch<256, true>(p, stream);
   return p.causal ? launch<128, true>(p, stream) : launch<128, false>(p, stream);
 }
 
