@@ -109,14 +109,18 @@ struct Tile {
   }
 };
 
-// POS: the scale is >= 0, so the block extreme of the raw scores is their
-// max (a negative scale needs their min).  Causal d = 64 is held to 128
-// registers so two workgroups share a CU (four waves per SIMD; its LDS
-// stages take 64 KiB); the other variants run one workgroup per CU.  ROPE:
-// 0 none; 1 Q rows are rotated by the rotary table as they are loaded (K
-// arrives rotated); 2 Q and every K stage are rotated.
-template <int D, bool CAUSAL, bool POS, int ROPE>
-__global__ __launch_bounds__(Cfg<D>::kThreads, (D == 64 && CAUSAL && ROPE < 2) ? 4 : 1) void prefill_bf16_kernel(PrefillParams p) {
+// One kernel serves causal and non-causal calls: the mask is a per-sequence
+// offset (row i sees keys j <= i + diag; diag = n - S_q for the bottom-right
+// causal mask, n for none), which compiles to fewer registers than separate
+// non-causal instances (those spilled at d = 256 and ran 8-15% slower at
+// d = 64 and 128).  POS: the scale is >= 0, so the block extreme of the raw
+// scores is their max (a negative scale needs their min).  d = 64 is held
+// to 128 registers so two workgroups share a CU (four waves per SIMD; its
+// LDS stages take 64 KiB); the other variants run one workgroup per CU.
+// ROPE: 0 none; 1 Q rows are rotated by the rotary table as they are loaded
+// (K arrives rotated); 2 Q and every K stage are rotated.
+template <int D, bool POS, int ROPE>
+__global__ __launch_bounds__(Cfg<D>::kThreads, (D == 64 && ROPE < 2) ? 4 : 1) void prefill_bf16_kernel(PrefillParams p) {
   using T = Tile<D>;
   constexpr int kThreads = Cfg<D>::kThreads;
   constexpr int kRows = Cfg<D>::kRows;
@@ -149,7 +153,7 @@ __global__ __launch_bounds__(Cfg<D>::kThreads, (D == 64 && CAUSAL && ROPE < 2) ?
   // Causal and paired: workgroup pair index pr covers tiles n_qt-1-pr then
   // pr (one tile when they coincide); causal unpaired: tile n_qt-1-pr
   // (heaviest first); non-causal: tile pr.
-  const bool pair = CAUSAL && p.pair != 0;
+  const bool pair = p.causal != 0 && p.pair != 0;
   const int n_pr = pair ? (n_qt + 1) / 2 : n_qt;
   int pr, h, b;
   if ((p.B * p.Hkv) % kXcds == 0) {
@@ -240,20 +244,17 @@ __global__ __launch_bounds__(Cfg<D>::kThreads, (D == 64 && CAUSAL && ROPE < 2) ?
 
   const int n_pass = (pair && n_qt_b - 1 - pr != pr) ? 2 : 1;
   for (int pass = 0; pass < n_pass; ++pass) {
-  const int qt = CAUSAL ? (pass == 0 ? n_qt_b - 1 - pr : pr) : pr;   // unpaired: pass 0 only
+  const int qt = pass == 0 ? n_qt_b - 1 - pr : pr;   // unpaired: pass 0 only
   const int tile_row0 = qt * kRows;
   const int wave_row0 = tile_row0 + wave * 32;
   const int my_row = wave_row0 + col;
   const int last_row = min(tile_row0 + kRows, sq) - 1;
-  // diag: row i sees keys j <= i + diag (bottom-right causal: n - sq); d =
-  // 256 runs non-causal calls through this instance with diag = n, which
-  // lets every row see every key.
-  const int diag = (CAUSAL && (D != 256 || p.causal != 0)) ? n - sq : n;
-  int kend = n;
-  if (CAUSAL) kend = min(n, max(0, last_row + diag + 1));
+  // row i sees keys j <= i + diag: bottom-right causal, or every key
+  const int diag = p.causal != 0 ? n - sq : n;
+  const int kend = min(n, max(0, last_row + diag + 1));
   const int n_blocks = (kend + kKeys - 1) / kKeys;
   const int wave_last_row = min(wave_row0 + 31, sq - 1);
-  const int my_last = CAUSAL ? my_row + diag : n - 1;   // last key this row sees
+  const int my_last = my_row + diag;   // last key this row sees (>= n - 1 without a mask)
 
   // Q^T as the B operand: lane (col, half) holds Q[my_row][16*ks + 8*half .. +7].
   bf16x8 qreg[KS];
@@ -512,11 +513,11 @@ __global__ __launch_bounds__(Cfg<D>::kThreads, (D == 64 && CAUSAL && ROPE < 2) ?
   // the sequence's end (in a partial last tile) computes nothing; it still
   // takes part in the copies and barriers.
   auto active = [&](int blk) {
-    return wave_row0 < sq && blk < n_blocks && blk * kKeys <= (CAUSAL ? wave_last_row + diag : n - 1);
+    return wave_row0 < sq && blk < n_blocks && blk * kKeys <= wave_last_row + diag;
   };
   auto needs_mask = [&](int blk) {
     const int j0 = blk * kKeys;
-    return (j0 + kKeys > n) || (CAUSAL && j0 + kKeys - 1 > wave_row0 + diag);
+    return (j0 + kKeys > n) || (j0 + kKeys - 1 > wave_row0 + diag);
   };
 
   // ---- the key loop ------------------------------------------------------
@@ -620,22 +621,22 @@ __global__ __launch_bounds__(Cfg<D>::kThreads, (D == 64 && CAUSAL && ROPE < 2) ?
 
 }
 
-template <int D, bool CAUSAL>
+template <int D>
 hipError_t launch(const PrefillParams& p, hipStream_t stream) {
   const int n_qt = (p.Sq + Cfg<D>::kRows - 1) / Cfg<D>::kRows;
-  const int n_pr = (CAUSAL && p.pair) ? (n_qt + 1) / 2 : n_qt;
+  const int n_pr = (p.causal && p.pair) ? (n_qt + 1) / 2 : n_qt;
   dim3 grid((unsigned)n_pr * p.Hq * p.B);
   const dim3 block(Cfg<D>::kThreads);
   const bool pos = p.scale_log2 >= 0.f;
   if (p.rope && p.rope_k) {
-    if (pos) hipLaunchKernelGGL((prefill_bf16_kernel<D, CAUSAL, true, 2>), grid, block, 0, stream, p);
-    else hipLaunchKernelGGL((prefill_bf16_kernel<D, CAUSAL, false, 2>), grid, block, 0, stream, p);
+    if (pos) hipLaunchKernelGGL((prefill_bf16_kernel<D, true, 2>), grid, block, 0, stream, p);
+    else hipLaunchKernelGGL((prefill_bf16_kernel<D, false, 2>), grid, block, 0, stream, p);
   } else if (p.rope) {
-    if (pos) hipLaunchKernelGGL((prefill_bf16_kernel<D, CAUSAL, true, 1>), grid, block, 0, stream, p);
-    else hipLaunchKernelGGL((prefill_bf16_kernel<D, CAUSAL, false, 1>), grid, block, 0, stream, p);
+    if (pos) hipLaunchKernelGGL((prefill_bf16_kernel<D, true, 1>), grid, block, 0, stream, p);
+    else hipLaunchKernelGGL((prefill_bf16_kernel<D, false, 1>), grid, block, 0, stream, p);
   } else {
-    if (pos) hipLaunchKernelGGL((prefill_bf16_kernel<D, CAUSAL, true, 0>), grid, block, 0, stream, p);
-    else hipLaunchKernelGGL((prefill_bf16_kernel<D, CAUSAL, false, 0>), grid, block, 0, stream, p);
+    if (pos) hipLaunchKernelGGL((prefill_bf16_kernel<D, true, 0>), grid, block, 0, stream, p);
+    else hipLaunchKernelGGL((prefill_bf16_kernel<D, false, 0>), grid, block, 0, stream, p);
   }
   return hipGetLastError();
 }
@@ -643,9 +644,9 @@ hipError_t launch(const PrefillParams& p, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_prefill_bf16(const PrefillParams& p, hipStream_t stream) {
-  if (p.d == 64) return p.causal ? launch<64, true>(p, stream) : launch<64, false>(p, stream);
-  if (p.d == 256) return launch<256, true>(p, stream);
-  return p.causal ? launch<128, true>(p, stream) : launch<128, false>(p, stream);
+  if (p.d == 64) return launch<64>(p, stream);
+  if (p.d == 256) return launch<256>(p, stream);
+  return launch<128>(p, stream);
 }
 
 }  // namespace attn

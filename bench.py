@@ -446,7 +446,7 @@ def main():
     roof_p = {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS,
               "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
               "traffic": measured_traffic(wp.name, "prefill"), "traffic_unit": "bytes/launch",
-              "kernel": "prefill_bf16_kernel<128, true, true, 0>", "avg_launch_ms": round(ms_p, 4),
+              "kernel": "prefill_bf16_kernel<128, true, 0>", "avg_launch_ms": round(ms_p, 4),
               "algorithmic_per_launch": flops_p}
     roof_d = {"bound": "hbm", "achieved": round(gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
               "frac": round(gbps / PEAK_HBM_GBPS, 4),
