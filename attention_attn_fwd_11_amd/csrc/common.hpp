@@ -85,6 +85,16 @@ __device__ __forceinline__ void global_to_lds16(const void* g, void* lds_base) {
   __builtin_amdgcn_global_load_lds(g, (lds_void*)lds_base, 16, 0, 0);
 }
 
+// Streaming forms of the 16-byte loads for data read exactly once (decode's
+// K and V): the nontemporal hint ("nt") reaches ~7 TB/s on an MI355X against
+// ~6.2 TB/s for ordinary loads in a streaming-read probe.
+__device__ __forceinline__ u32x4 ld16_stream(const void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
+__device__ __forceinline__ void global_to_lds16_stream(const void* g, void* lds_base) {
+  __builtin_amdgcn_global_load_lds(g, (lds_void*)lds_base, 16, 0, 2);   // cache policy 2: nt
+}
+
 // Buffer resource over `bytes` bytes starting at `base`, raw (unformatted)
 // dword access: word 3 = 0x00020000 selects the 32-bit data format with no
 // swizzle and no index stride.  Reads at or past `bytes` return zero.

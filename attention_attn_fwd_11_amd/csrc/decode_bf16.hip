@@ -107,12 +107,12 @@ __global__ __launch_bounds__(kThreads) void decode_split_valu(DecodeParams p) {
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       const int key = min(base + u * KPI + kg, c1 - 1) - base;
-      kr[u] = ld16(kp + key * D + 8 * dc);
+      kr[u] = ld16_stream(kp + key * D + 8 * dc);
     }
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       const int key = min(base + u * KPI + kg, c1 - 1) - base;
-      vr[u] = ld16(vp + key * D + 8 * dc);
+      vr[u] = ld16_stream(vp + key * D + 8 * dc);
     }
     // partial dots over this lane's 8 features
     float part[8];
@@ -290,22 +290,22 @@ __global__ __launch_bounds__(kThreads, 3) void decode_split_mfma(DecodeParams p)
 #pragma unroll
       for (int hlf = 0; hlf < 2; ++hlf)
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) kr[hlf][ks] = ld16(kb + k_off + hlf * 16 * D * 2 + ks * 64);
+        for (int ks = 0; ks < KS; ++ks) kr[hlf][ks] = ld16_stream(kb + k_off + hlf * 16 * D * 2 + ks * 64);
 #pragma unroll
-      for (int u = 0; u < VP; ++u) vr[u] = ld16(vbs + lane * 16 + u * 1024);
+      for (int u = 0; u < VP; ++u) vr[u] = ld16_stream(vbs + lane * 16 + u * 1024);
     } else {
 #pragma unroll
       for (int hlf = 0; hlf < 2; ++hlf) {
         const int key = min(base + 16 * hlf + qcol, c1 - 1) - base;
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) kr[hlf][ks] = ld16(kp + key * D + 32 * ks + 8 * grp);
+        for (int ks = 0; ks < KS; ++ks) kr[hlf][ks] = ld16_stream(kp + key * D + 32 * ks + 8 * grp);
       }
 #pragma unroll
       for (int u = 0; u < VP; ++u) {
         const int piece = u * 64 + lane;
         const int row = piece / SLOTS, slot = piece % SLOTS;
         const int key = min(base + row, c1 - 1) - base;
-        vr[u] = ld16(vp + key * D + slot * 8);
+        vr[u] = ld16_stream(vp + key * D + slot * 8);
       }
     }
     // S^T for keys [base, base+16) and [base+16, base+32)
@@ -548,21 +548,21 @@ __global__ __launch_bounds__(kThreads, 3) void decode_split_balanced(DecodeParam
 #pragma unroll
         for (int hlf = 0; hlf < 2; ++hlf)
 #pragma unroll
-          for (int ks = 0; ks < KS; ++ks) kr[hlf][ks] = ld16(kb + k_off + hlf * 16 * D * 2 + ks * 64);
+          for (int ks = 0; ks < KS; ++ks) kr[hlf][ks] = ld16_stream(kb + k_off + hlf * 16 * D * 2 + ks * 64);
 #pragma unroll
         for (int w = 0; w < VP; ++w)
-          global_to_lds16(vbs + (v_row0 + w * kRowsPerCopy) * 2 * D + v_slot(w) * 16, vb + w * 1024);
+          global_to_lds16_stream(vbs + (v_row0 + w * kRowsPerCopy) * 2 * D + v_slot(w) * 16, vb + w * 1024);
       } else {
 #pragma unroll
         for (int hlf = 0; hlf < 2; ++hlf) {
           const int key = min(base + 16 * hlf + qcol, n - 1) - base;
 #pragma unroll
-          for (int ks = 0; ks < KS; ++ks) kr[hlf][ks] = ld16(kp + key * D + 32 * ks + 8 * grp);
+          for (int ks = 0; ks < KS; ++ks) kr[hlf][ks] = ld16_stream(kp + key * D + 32 * ks + 8 * grp);
         }
 #pragma unroll
         for (int w = 0; w < VP; ++w) {
           const int key = min(base + v_row0 + w * kRowsPerCopy, n - 1) - base;
-          global_to_lds16(reinterpret_cast<const char*>(vp + key * D) + v_slot(w) * 16,
+          global_to_lds16_stream(reinterpret_cast<const char*>(vp + key * D) + v_slot(w) * 16,
                           vb + w * 1024);
         }
       }

@@ -147,9 +147,10 @@ def cpu_baseline(w, x, seconds):
 
 
 def read_probe(torch, dev, gib=4):
-    """Streaming-read ceiling on this device: the plain grid-stride read kernel
-    of libattn_probe.so over `gib` GiB, best over a few launch shapes.  Context
-    for the decode figures; the roofline peak stays the published 8 TB/s."""
+    """Streaming-read ceiling on this device: the grid-stride nontemporal read
+    kernel of libattn_probe.so over `gib` GiB, best over a few launch shapes.
+    Context for the decode figures; the roofline peak stays the published
+    8 TB/s."""
     import ctypes
     lib = ctypes.CDLL(os.path.join(ROOT, "attention_attn_fwd_11_amd", "libattn_probe.so"))
     lib.attn_probe_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
@@ -158,7 +159,7 @@ def read_probe(torch, dev, gib=4):
     lib.attn_probe_out_words.restype = ctypes.c_size_t
     nbytes = gib << 30
     buf = torch.ones(nbytes // 4, dtype=torch.int32, device=dev)
-    shapes = [2048, 8192, 16384]
+    shapes = [8192, 16384, 32768]
     out = torch.empty(lib.attn_probe_out_words(max(shapes)), dtype=torch.int32, device=dev)
     stream = torch.cuda.current_stream().cuda_stream
     best = {}
@@ -179,7 +180,7 @@ def read_probe(torch, dev, gib=4):
     del buf, out
     blocks = max(best, key=best.get)
     return {"gbps": round(best[blocks], 1), "bytes": nbytes, "workgroups": blocks,
-            "kernel": "grid-stride 16-byte loads, 4 in flight per lane (libattn_probe.so)"}
+            "kernel": "grid-stride 16-byte nontemporal loads, 8 in flight per lane (libattn_probe.so)"}
 
 
 def varlen_prefill(torch, attn, wl, dev, steps, warmup):
