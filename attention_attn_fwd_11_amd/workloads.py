@@ -73,6 +73,8 @@ WORKLOADS = [
              note="causal prefill at head dimension 64"),
     Workload("prefill_bf16_b4h16s4096_d256", "prefill", 4, 16, 16, 4096, 4096, 256, "bf16", True,
              note="causal prefill at head dimension 256 (the headline's FLOPs with half the heads)"),
+    Workload("prefill_noncausal_bf16_b4h32s4096", "prefill", 4, 32, 32, 4096, 4096, 128, "bf16",
+             False, note="non-causal prefill (every query sees every key)"),
     Workload("prefill_chunked_gqa_bf16_b16h32kv8q512", "prefill", 16, 32, 8, 512, 8192, 128,
              "bf16", True, len_range=(512, 8192),
              note="chunked prefill: 512 new tokens per sequence over a ragged KV cache "

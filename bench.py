@@ -386,7 +386,7 @@ def main():
     others = [] if args.no_others else [wl.BY_NAME[n] for n in (
         "decode_gqa_bf16_b128h32kv8", "prefill_gqa_bf16_h64kv8s16384",
         "prefill_bf16_b4h32s4096_d64", "prefill_bf16_b4h16s4096_d256",
-        "prefill_chunked_gqa_bf16_b16h32kv8q512")]
+        "prefill_chunked_gqa_bf16_b16h32kv8q512", "prefill_noncausal_bf16_b4h32s4096")]
     inputs = {w.name: wl.generate(w, dev) for w in [wp, wd, *others]}
     torch.cuda.synchronize()
 

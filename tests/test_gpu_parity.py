@@ -328,7 +328,8 @@ def test_side_stream_ordering():
 # ---------------------------------------------------------------------------
 @pytest.mark.parametrize("name", ["prefill_bf16_b4h32s4096", "prefill_gqa_bf16_h64kv8s16384",
                                   "prefill_bf16_b4h32s4096_d64", "prefill_bf16_b4h16s4096_d256",
-                                  "prefill_chunked_gqa_bf16_b16h32kv8q512"])
+                                  "prefill_chunked_gqa_bf16_b16h32kv8q512",
+                                  "prefill_noncausal_bf16_b4h32s4096"])
 def test_prefill_workload_sampled(name):
     w = wl.BY_NAME[name]
     say(f"workload {name}: {w.describe()}")
