@@ -33,10 +33,22 @@ FLAGS = [
 ]
 
 
+# Per-source device flags.  The prefill kernels at d = 256 need more than
+# 256 registers per lane; by default the compiler puts the MFMA output
+# accumulator in the accumulation registers and copies it into vector
+# registers on every K/V stage (for the rare rescale of the accumulator).
+# MFMA results in vector registers leave the accumulation registers to
+# values the matrix cores only read, with no copies and no spills.
+SOURCE_FLAGS = {
+    "prefill_bf16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+}
+
+
 def _compile(src, extra):
     out = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
     lang = ["-x", "hip"] if src.endswith(".cpp") else []
-    cmd = [HIPCC, *FLAGS, *extra, *lang, "-c", os.path.join(CSRC, src), "-o", out]
+    cmd = [HIPCC, *FLAGS, *SOURCE_FLAGS.get(src, []), *extra, *lang, "-c", os.path.join(CSRC, src),
+           "-o", out]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}{r.stderr}")

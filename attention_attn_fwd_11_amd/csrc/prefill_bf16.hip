@@ -456,7 +456,7 @@ __global__ __launch_bounds__(Cfg<D>::kThreads, (D == 64 && ROPE < 2) ? 4 : 1) vo
     }
     const float tmax = (MASKED && traw == neutral) ? kNegInf : traw * c;
     const float cand = fmaxf(mref, tmax);
-    if (__any(cand > mref + kRescaleSlack)) {
+    if (__builtin_expect(__any(cand > mref + kRescaleSlack), 0)) {
       const float alpha = cand == kNegInf ? 1.f : exp2_fast(mref - cand);
       mref = cand;
       lsum *= alpha;
@@ -538,7 +538,7 @@ __global__ __launch_bounds__(Cfg<D>::kThreads, (D == 64 && ROPE < 2) ? 4 : 1) vo
         // only computed on that rare path.  The result is the one prepare +
         // probabilities would give.
         float psum = probabilities(std::false_type{}, sc, pb);
-        if (__any(!(psum <= kLazyLimit))) {
+        if (__builtin_expect(__any(!(psum <= kLazyLimit)), 0)) {
           const float m_old = mref;
           prepare(std::false_type{}, sc, blk * kKeys);
           if (__any(mref != m_old)) psum = probabilities(std::false_type{}, sc, pb);
