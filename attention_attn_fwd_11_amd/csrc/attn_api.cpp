@@ -302,7 +302,13 @@ attn_status_t attn_prefill_varlen_fwd(const void* q, const void* k, const void* 
   p.q = q; p.k = k; p.v = v; p.o = o; p.kv_lens = nullptr;
   p.B = B; p.Hq = H_q; p.Hkv = H_kv; p.Sq = max_seqlen_q; p.Skv = max_seqlen_k; p.d = d;
   p.causal = causal;
-  p.pair = pair_tiles(causal, max_seqlen_q, max_seqlen_k);
+  // Pairs even out the tiles of one sequence, but over sequences of unequal
+  // lengths single tiles, heaviest first, balance the grid better (16
+  // sequences of U[256, 4096] tokens: 1.110 -> 0.987 ms).  Every sequence has
+  // the maximum lengths exactly when the totals say so.
+  const bool uniform = (int64_t)total_q == (int64_t)B * max_seqlen_q &&
+                       (int64_t)total_k == (int64_t)B * max_seqlen_k;
+  p.pair = uniform ? pair_tiles(causal, max_seqlen_q, max_seqlen_k) : 0;
   p.scale_log2 = (float)((double)scale * 1.4426950408889634);
   p.cu_q = cu_seqlens_q; p.cu_k = cu_seqlens_k; p.total_q = total_q; p.total_k = total_k;
   hipError_t e = attn::launch_prefill_bf16(p, s);
