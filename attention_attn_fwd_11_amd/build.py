@@ -19,8 +19,8 @@ LIB = os.path.join(PKG, "libattn.so")
 PROBE_LIB = os.path.join(PKG, "libattn_probe.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["attn_api.cpp", "prefill_f32.hip", "prefill_bf16.hip", "decode_bf16.hip", "util.hip",
-           "rope_bf16.hip"]
+SOURCES = ["attn_api.cpp", "prefill_f32.hip", "prefill_bf16.hip", "prefill_d256.hip", "decode_bf16.hip",
+           "util.hip", "rope_bf16.hip"]
 PROBE_SOURCES = ["read_probe.hip"]
 
 # Device code for gfx950 only.  Packed-fp32 instruction selection is switched
@@ -41,6 +41,7 @@ FLAGS = [
 # values the matrix cores only read, with no copies and no spills.
 SOURCE_FLAGS = {
     "prefill_bf16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+    "prefill_d256.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
 }
 
 

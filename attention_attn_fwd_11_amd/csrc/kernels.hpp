@@ -68,6 +68,8 @@ constexpr int kDecodeUnit = 128;
 
 hipError_t launch_prefill_f32(const PrefillParams& p, hipStream_t stream);
 hipError_t launch_prefill_bf16(const PrefillParams& p, hipStream_t stream);
+// d = 256 without the rotary embedding (16-row waves; called by launch_prefill_bf16)
+hipError_t launch_prefill_d256(const PrefillParams& p, hipStream_t stream);
 hipError_t launch_decode_bf16(const DecodeParams& p, hipStream_t stream);
 hipError_t launch_zero_fill(void* dst, size_t bytes, hipStream_t stream);
 // Rotary embedding of key rows into dst (same [B, H, S, d] bf16 layout as

@@ -645,7 +645,8 @@ hipError_t launch(const PrefillParams& p, hipStream_t stream) {
 
 hipError_t launch_prefill_bf16(const PrefillParams& p, hipStream_t stream) {
   if (p.d == 64) return launch<64>(p, stream);
-  if (p.d == 256) return launch<256>(p, stream);
+  // d = 256 without the rotary embedding: 16-row waves, two per SIMD
+  if (p.d == 256) return p.rope ? launch<256>(p, stream) : launch_prefill_d256(p, stream);
   return launch<128>(p, stream);
 }
 

@@ -109,8 +109,16 @@ def test_identity_table_equals_plain_prefill(d):
                       rope_workspace=workspace(B, Hkv, S, d))
     b = attn.prefill(x["q"], x["k"], x["v"], causal=True)
     torch.cuda.synchronize()
-    assert torch.equal(a, b), "cos 1 / sin 0 must leave Q and K unchanged"
-    assert torch.equal(a2, b), "cos 1 / sin 0 must leave Q and K unchanged (pre-pass)"
+    assert torch.equal(a, a2), "K rotated in the kernel and by the pre-pass must give the same bits"
+    if d < 256:
+        # the rotary and the plain calls run the same kernel: bit equality
+        assert torch.equal(a, b), "cos 1 / sin 0 must leave Q and K unchanged"
+    else:
+        # at d = 256 the plain call runs the 16-row kernel, the rotary calls the
+        # 32-row one (different summation orders): both against the definition
+        ref = oracle.attention(x["q"].cpu(), x["k"].cpu(), x["v"].cpu(), True, 1.0 / np.sqrt(d))
+        assert_close(a, ref, torch.bfloat16, "rope identity table d256")
+        assert_close(b, ref, torch.bfloat16, "plain d256")
 
 
 def test_rope_equals_host_rotation_then_plain_prefill():
