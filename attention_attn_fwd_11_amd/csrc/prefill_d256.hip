@@ -60,6 +60,14 @@ constexpr int kMaxRankB = 256;
 constexpr float kRescaleSlack = 8.f;
 constexpr float kLazyLimit = 256.f;
 static_assert(kCopyRows % 16 == 0, "every copy round starts on the same swizzle phase");
+// LDS reads in flight ahead of the MFMAs that consume them: K fragments one
+// k-step (four MFMAs) ahead, V^T fragments four MFMAs ahead; each MFMA with
+// the reads issued beside it is one scheduling region, so the distances hold
+// (left to the scheduler, each P V MFMA waited on reads issued one MFMA
+// earlier).  Measured for B4 H16 S4096: 0.647 -> 0.620 ms; deeper rings (two
+// k-steps, six or eight MFMAs) were no faster.
+constexpr int KPF = 1;
+constexpr int VPF = 4;
 
 __device__ __forceinline__ int sw(int r) { return ((r & 7) << 1) | ((r >> 3) & 1); }
 // byte offset of (row, 16-byte slot) inside a swizzled stage
@@ -242,24 +250,27 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_d256_kernel(PrefillParams
   const float c = p.scale_log2;
   constexpr float neutral = POS ? kNegInf : kPosInf;
 
-  // S^T of a 64-key block: four 16-key tiles, K fragments read one k-step ahead.
+  // S^T of a 64-key block: four 16-key tiles, K fragments read KPF k-steps ahead.
   auto scores = [&](auto st_c, f32x4 (&sacc)[4]) {
     const unsigned char* kb = kbuf(st_c);
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt) sacc[kt] = f32x4{};
-    u32x4 a[2][4];
+    u32x4 a[KPF + 1][4];
 #pragma unroll
-    for (int kt = 0; kt < 4; ++kt) a[0][kt] = *reinterpret_cast<const u32x4*>(kb + kt * 16 * kRowBytes + k_off[0]);
+    for (int ks = 0; ks < KPF; ++ks)
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt) a[ks][kt] = *reinterpret_cast<const u32x4*>(kb + kt * 16 * kRowBytes + k_off[ks]);
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      if (ks + 1 < KS) {
+      if (ks + KPF < KS) {
 #pragma unroll
         for (int kt = 0; kt < 4; ++kt)
-          a[(ks + 1) & 1][kt] = *reinterpret_cast<const u32x4*>(kb + kt * 16 * kRowBytes + k_off[ks + 1]);
+          a[(ks + KPF) % (KPF + 1)][kt] = *reinterpret_cast<const u32x4*>(kb + kt * 16 * kRowBytes + k_off[ks + KPF]);
       }
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt)
-        sacc[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a[ks & 1][kt]), qreg[ks], sacc[kt], 0, 0, 0);
+        sacc[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a[ks % (KPF + 1)][kt]), qreg[ks], sacc[kt], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);     // keep the reads KPF k-steps ahead
     }
   };
 
@@ -324,18 +335,27 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_d256_kernel(PrefillParams
     return psum;
   };
 
-  // O^T += V^T P^T; V^T from transpose reads of the row-major V stage.
+  // O^T += V^T P^T; V^T from transpose reads of the row-major V stage,
+  // issued VPF MFMAs ahead (a 16-cycle MFMA is far shorter than an LDS read).
   auto accumulate = [&](auto st_c, const u32x4 (&pb)[2]) {
     const unsigned char* vb = vbuf(st_c);
+    constexpr int NM = 2 * DT;
+    auto vread = [&](int m) {
+      const int kk = m / DT, t = m % DT;
+      const u32x2 lo = lds_read_tr16x4(vb + kk * 32 * kRowBytes + v_lo[t]);
+      const u32x2 hi = lds_read_tr16x4(vb + kk * 32 * kRowBytes + v_hi[t]);
+      return u32x4{lo[0], lo[1], hi[0], hi[1]};
+    };
+    u32x4 vf[VPF + 1];
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
+    for (int m = 0; m < VPF; ++m) vf[m] = vread(m);
 #pragma unroll
-      for (int t = 0; t < DT; ++t) {
-        const u32x2 lo = lds_read_tr16x4(vb + kk * 32 * kRowBytes + v_lo[t]);
-        const u32x2 hi = lds_read_tr16x4(vb + kk * 32 * kRowBytes + v_hi[t]);
-        oacc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]}),
-                                                          as_bf16x8(pb[kk]), oacc[t], 0, 0, 0);
-      }
+    for (int m = 0; m < NM; ++m) {
+      if (m + VPF < NM) vf[(m + VPF) % (VPF + 1)] = vread(m + VPF);
+      const int kk = m / DT, t = m % DT;
+      oacc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(vf[m % (VPF + 1)]), as_bf16x8(pb[kk]), oacc[t],
+                                                        0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);   // keep the reads VPF MFMAs ahead
     }
   };
 
