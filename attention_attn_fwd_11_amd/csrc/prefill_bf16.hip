@@ -500,21 +500,30 @@ __global__ __launch_bounds__(Cfg<D>::kThreads, (D == 64 && ROPE < 2) ? 4 : 1) vo
 
   // O^T += V^T P^T from LDS stage S; V^T comes from transpose reads of the
   // row-major block (k-step outer, output tile inner: DT independent chains).
-  auto accumulate = [&](auto stage_c, auto sub_c, const u32x4 (&pb)[4]) {
+  constexpr int PF = kVAhead;
+  auto vread = [&](auto stage_c, auto sub_c, int m) {
     const unsigned char* vb = vbuf(stage_c) + decltype(sub_c)::value * T::kSubBytes;
-    constexpr int NM = 4 * DT, PF = kVAhead;
-    auto vread = [&](int m) {
-      const int cc = m / DT, t = m % DT;
-      const u32x2 lo = lds_read_tr16x4(vb + cc * 16 * T::kRowBytes + v_lo[t]);
-      const u32x2 hi = lds_read_tr16x4(vb + cc * 16 * T::kRowBytes + v_hi[t]);
-      return u32x4{lo[0], lo[1], hi[0], hi[1]};
-    };
-    u32x4 vf[PF + 1];
+    const int cc = m / DT, t = m % DT;
+    const u32x2 lo = lds_read_tr16x4(vb + cc * 16 * T::kRowBytes + v_lo[t]);
+    const u32x2 hi = lds_read_tr16x4(vb + cc * 16 * T::kRowBytes + v_hi[t]);
+    return u32x4{lo[0], lo[1], hi[0], hi[1]};
+  };
+  // The first PF fragments.  At d = 128 and 256 they are read before the
+  // softmax, whose vector work then covers their latency (headline shape
+  // 0.559 -> 0.551 ms, non-causal 0.994 -> 0.974); at d = 64, held to 128
+  // registers, that would spill, so there they are read at the start of P V
+  // (so too with K rotated in the kernel, which holds the table rows).
+  constexpr bool kEarlyV = D != 64 && ROPE != 2;
+  auto v_first = [&](auto stage_c, auto sub_c, u32x4 (&vf)[PF + 1]) {
 #pragma unroll
-    for (int m = 0; m < PF; ++m) vf[m] = vread(m);
+    for (int m = 0; m < PF; ++m) vf[m] = vread(stage_c, sub_c, m);
+  };
+  auto accumulate = [&](auto stage_c, auto sub_c, const u32x4 (&pb)[4], u32x4 (&vf)[PF + 1]) {
+    constexpr int NM = 4 * DT;
+    if constexpr (!kEarlyV) v_first(stage_c, sub_c, vf);
 #pragma unroll
     for (int m = 0; m < NM; ++m) {
-      if (m + PF < NM) vf[(m + PF) % (PF + 1)] = vread(m + PF);
+      if (m + PF < NM) vf[(m + PF) % (PF + 1)] = vread(stage_c, sub_c, m + PF);
       const int cc = m / DT, t = m % DT;
       oacc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vf[m % (PF + 1)]), as_bf16x8(pb[cc]), oacc[t], 0, 0, 0);
       __builtin_amdgcn_sched_barrier(0);
@@ -543,7 +552,12 @@ __global__ __launch_bounds__(Cfg<D>::kThreads, (D == 64 && ROPE < 2) ? 4 : 1) vo
     if (active(blk)) {
       f32x16 sc[2];
       u32x4 pb[4];
+      u32x4 vf[PF + 1];
       scores(st_c, sub_c, sc);
+      if constexpr (kEarlyV) {
+        v_first(st_c, sub_c, vf);
+        __builtin_amdgcn_sched_barrier(0);
+      }
       if (!needs_mask(blk)) {
         // P against the current reference first: the rescale is due only if
         // some P exceeds 2^kRescaleSlack, and then this lane's sum of P does
@@ -562,7 +576,7 @@ __global__ __launch_bounds__(Cfg<D>::kThreads, (D == 64 && ROPE < 2) ? 4 : 1) vo
         lsum += probabilities(std::true_type{}, sc, pb);
       }
       __builtin_amdgcn_sched_barrier(0);
-      accumulate(st_c, sub_c, pb);
+      accumulate(st_c, sub_c, pb, vf);
     }
   };
   auto stage_step = [&](auto st_c, int sb) {
