@@ -92,6 +92,23 @@ def test_prefill_matches_oracle(case):
     assert_close(o, ref, x["q"].dtype, f"prefill {case}")
 
 
+@pytest.mark.parametrize("d", [64, 128, 256])
+def test_prefill_more_sequences_than_the_ranked_order_covers(d):
+    """Above 256 sequences the kernels keep the launch order (no longest-first
+    ranking); ragged lengths, empty sequences and both XCD tile maps
+    (B * H_kv = 260, not a multiple of 8, and 520, one) must stay exact."""
+    g = np.random.default_rng(70 + d)
+    for B, Hkv in [(260, 1), (260, 2)]:
+        lens = [int(n) for n in g.integers(0, 41, size=B)]
+        say(f"prefill B{B} Hkv{Hkv} d{d} ragged lengths, unranked")
+        x = make(B, 2 * Hkv, Hkv, 40, 40, d, seed=d + Hkv)
+        scale = 1.0 / np.sqrt(d)
+        o = attn.prefill(x["q"], x["k"], x["v"], causal=True, scale=scale, kv_lens=lens_tensor(lens))
+        torch.cuda.synchronize()
+        ref = oracle.attention(x["q"].cpu(), x["k"].cpu(), x["v"].cpu(), True, scale, kv_lens=lens)
+        assert_close(o, ref, torch.bfloat16, f"prefill B{B} Hkv{Hkv} d{d} unranked")
+
+
 def test_prefill_workload_f32_small_full():
     w = wl.BY_NAME["prefill_f32_small"]
     say(f"workload {w.name}: {w.describe()}")

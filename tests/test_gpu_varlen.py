@@ -50,6 +50,35 @@ def test_varlen_matches_oracle(case):
         assert_close(got, ref, torch.bfloat16, f"varlen {case} sequence {b}")
 
 
+@pytest.mark.parametrize("d", [128, 256])
+def test_varlen_more_sequences_than_the_ranked_order_covers(d):
+    """260 packed sequences (above the 256 the kernels rank longest first),
+    some with no query or no key, against the oracle per sequence."""
+    g = np.random.default_rng(80 + d)
+    q_lens = [int(n) for n in g.integers(0, 50, size=260)]
+    k_lens = [int(n) for n in g.integers(0, 60, size=260)]
+    print(f"varlen 260 sequences d{d}", flush=True)
+    x = wl.varlen_problem(q_lens, k_lens, 4, 2, d, device=DEV, seed=33)
+    scale = 1.0 / np.sqrt(d)
+    o = attn.prefill_varlen(x["q"], x["k"], x["v"], x["cu_q"], x["cu_k"], max(q_lens), max(k_lens),
+                            causal=True, scale=scale)
+    torch.cuda.synchronize()
+    cq, ck = x["cu_q"].tolist(), x["cu_k"].tolist()
+    q, k, v, oc = x["q"].cpu(), x["k"].cpu(), x["v"].cpu(), o.cpu()
+    for b, (s, n) in enumerate(zip(q_lens, k_lens)):
+        if s == 0:
+            continue
+        got = oc[cq[b]:cq[b + 1]].permute(1, 0, 2).unsqueeze(0)
+        if n == 0:
+            assert torch.count_nonzero(got) == 0, f"sequence {b} has no key: O must be 0"
+            continue
+        qb = q[cq[b]:cq[b + 1]].permute(1, 0, 2).unsqueeze(0).contiguous()
+        kb = k[ck[b]:ck[b + 1]].permute(1, 0, 2).unsqueeze(0).contiguous()
+        vb = v[ck[b]:ck[b + 1]].permute(1, 0, 2).unsqueeze(0).contiguous()
+        ref = oracle.attention(qb, kb, vb, True, scale)
+        assert_close(got, ref, torch.bfloat16, f"varlen 260 d{d} sequence {b}")
+
+
 @pytest.mark.parametrize("causal", [True, False])
 def test_varlen_equals_padded_for_equal_lengths(causal):
     B, Hq, Hkv, S, d = 3, 8, 2, 500, 128
