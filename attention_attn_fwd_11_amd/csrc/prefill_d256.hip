@@ -26,7 +26,11 @@
 //     slot s of row r is stored at s ^ sw(r), sw(r) = 2 (r & 7) | (r >> 3) & 1.
 //     The K-operand read (16 consecutive rows, one slot each) then covers all
 //     64 banks, and so does the transpose read of V (8 consecutive rows, one
-//     aligned slot pair each).
+//     aligned slot pair each) by address; the hardware still spends one extra
+//     pass on each transpose read of this layout, whose two 16-lane groups
+//     read different rows of the same columns (measured with two swizzles).
+//   - LDS reads are issued ahead of the MFMAs that consume them (K one
+//     k-step, V^T four MFMAs), each MFMA with its reads one scheduling region.
 //   - Softmax in base 2 with the scale folded into the exponent's FMA, lazy
 //     rescaling (the reference max moves only when a block max exceeds it by
 //     more than 2^8), P rounded to bf16 and summed from the rounded values.
