@@ -17,7 +17,9 @@
 //                            queries form a small matrix and QK^T and PV run on
 //                            v_mfma_f32_16x16x32_bf16 with the group padded to
 //                            16 rows.
-//   decode_combine<D>        merges the partials of one (batch, query head).
+//   decode_combine<D>        merges the partials of one (batch, query head);
+//                            not launched when every head has a single split
+//                            (decode_split_valu then writes O itself).
 //
 // Partial results are fp32; the log-sum-exp is kept in base-2 units
 // (scores are scaled by scale * log2(e)).  Chunks that start at or beyond a
@@ -84,7 +86,13 @@ __global__ __launch_bounds__(kThreads) void decode_split_valu(DecodeParams p) {
   int n = p.Skv;
   if (p.kv_lens) n = min(max(p.kv_lens[b], 0), p.Skv);
   const int c0 = split * p.chunk;
-  if (c0 >= n) return;
+  // One split per head: this workgroup writes O itself (no combine pass).
+  uint16_t* orow = static_cast<uint16_t*>(p.o) + ((int64_t)b * p.Hq + h) * D;
+  if (c0 >= n) {
+    if (p.n_split == 1)   // no key: O = 0
+      for (int d = threadIdx.x; d < D; d += kThreads) orow[d] = 0;
+    return;
+  }
   const int c1 = min(c0 + p.chunk, n);
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -211,9 +219,10 @@ __global__ __launch_bounds__(kThreads) void decode_split_valu(DecodeParams p) {
       float acc = 0.f;
 #pragma unroll
       for (int w = 0; w < kWaves; ++w) acc += wgt[w] * merge.o[w][d];
-      p.part_o[prow * D + d] = acc * invL;
+      if (p.n_split == 1) orow[d] = f32_to_bf16_bits(acc * invL);
+      else p.part_o[prow * D + d] = acc * invL;
     }
-    if (lane == 0) p.part_lse[prow] = M + log2_fast(L);
+    if (lane == 0 && p.n_split > 1) p.part_lse[prow] = M + log2_fast(L);
   }
 }
 
@@ -778,6 +787,7 @@ hipError_t launch_d(const DecodeParams& p, hipStream_t stream) {
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  if (G == 1 && p.n_split == 1) return hipSuccess;   // the split pass wrote O
   hipLaunchKernelGGL((decode_combine<D>), dim3(p.Hq, p.B), dim3(64), 0, stream, p);
   return hipGetLastError();
 }
