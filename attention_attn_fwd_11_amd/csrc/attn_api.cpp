@@ -75,13 +75,13 @@ int decode_chunk(int32_t B, int32_t H_q, int32_t H_kv, int32_t S_kv) {
     const long c = std::strtol(env, nullptr, 10);
     if (c >= 256 && c % 256 == 0 && c <= (1 << 30)) return (int)c;
   }
-  // Aim for about 2048 workgroups (8 per compute unit on a 256-CU part, two
-  // rounds of resident workgroups), but never split below 512 keys: each
-  // split costs a partial (d+1 floats) per query.  For B64 H32 L4096 one split
-  // per head (2048 workgroups) streams at 6.95 TB/s, two (4096) at 6.86, four
-  // at 6.75.
+  // Aim for about 4096 workgroups (16 per compute unit on a 256-CU part), so
+  // the cache of every head is split even at B64 H32, but never split below
+  // 512 keys: each split costs a partial (d+1 floats) per query.  (For B64
+  // H32 L4096 one split per head would stream at 6.95 TB/s, two, as chosen,
+  // at 6.86, four at 6.75.)
   const int64_t heads = (int64_t)B * H_kv;
-  int64_t splits = heads >= 2048 ? 1 : (2048 + heads - 1) / heads;
+  int64_t splits = heads >= 4096 ? 1 : (4096 + heads - 1) / heads;
   const int64_t max_splits = (S_kv + 511) / 512;
   if (splits > max_splits) splits = max_splits;
   if (splits < 1) splits = 1;
