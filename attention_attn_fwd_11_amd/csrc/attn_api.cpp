@@ -150,16 +150,15 @@ attn_status_t run_decode(const void* q, const void* k, const void* v, void* o, i
   p.n_split = (S_kv + p.chunk - 1) / p.chunk;
   p.n_wg = 0;
   if (decode_balanced(B, H_q, H_kv)) {
-    // Persistent grid: three resident workgroups per compute unit, never more
+    // Persistent grid: two workgroups per compute unit (the resident
+    // capacity: each stages a K and a V block per wave in LDS), never more
     // than there are units.  The contiguous and the paged cache use the same
-    // grid, so both partition the keys alike and give the same bits.  (With
-    // two per unit the contiguous GQA decode ran ~1.5% faster, 0.340 against
-    // 0.345 ms, the paged one ~3.5% slower, 0.368 against 0.355.)  Test-only
-    // override: ATTN_DECODE_WORKGROUPS.
+    // grid, so both partition the keys alike and give the same bits.
+    // Test-only override: ATTN_DECODE_WORKGROUPS.
     int dev = 0;
     const int cus = device_cus(&dev);
     if (cus <= 0) return hip_fail("hipDeviceGetAttribute(multiprocessor count)", hipGetLastError());
-    int64_t wg = 3 * (int64_t)cus;
+    int64_t wg = 2 * (int64_t)cus;
     if (const char* env = std::getenv("ATTN_DECODE_WORKGROUPS")) {
       const long w = std::strtol(env, nullptr, 10);
       if (w >= 1 && w <= (1 << 20)) wg = w;

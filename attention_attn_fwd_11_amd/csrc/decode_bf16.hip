@@ -35,6 +35,14 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
 
+// Waits until at most N of this wave's vector-memory loads are outstanding
+// (loads complete in issue order, so the earliest ones have landed).
+template <int N>
+__device__ __forceinline__ void wait_vmem_below() {
+  static_assert(N >= 0 && N < 64, "vmcnt takes 0..63");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
 // First element of key row j of head (b, hk) in tensor t (K or V): the
 // contiguous cache [B, Hkv, Skv, d], or the page that holds row j.  Every
 // step of the split kernels covers at most 64 keys starting at a multiple of
@@ -473,7 +481,7 @@ __device__ __forceinline__ void unit_prefix(const DecodeParams& p, int* pre, int
 }
 
 template <int D, int G>
-__global__ __launch_bounds__(kThreads, 3) void decode_split_balanced(DecodeParams p) {
+__global__ __launch_bounds__(kThreads, 2) void decode_split_balanced(DecodeParams p) {
   constexpr int KS = D / 32;          // k-steps of the score MFMA (32 features each)
   constexpr int DT = D / 16;          // 16-feature output tiles
   constexpr int SLOTS = D / 8;        // 16-byte slots per V row
@@ -482,6 +490,7 @@ __global__ __launch_bounds__(kThreads, 3) void decode_split_balanced(DecodeParam
 
   static_assert(kWaves * G * D * 4 <= kWaves * VBYTES, "merge buffer must fit the V buffers");
   __shared__ __attribute__((aligned(16))) unsigned char vbuf[kWaves][VBYTES];
+  __shared__ __attribute__((aligned(16))) unsigned char kbuf[kWaves][VBYTES];
   __shared__ float mrg_m[kWaves][16];
   __shared__ float mrg_l[kWaves][16];
   __shared__ int pre[kDecodeMaxBatch + 1];
@@ -499,7 +508,7 @@ __global__ __launch_bounds__(kThreads, 3) void decode_split_balanced(DecodeParam
   const int qcol = lane & 15;          // query column (valid if < G)
   const int grp = lane >> 4;           // 16-lane group
   unsigned char* vb = vbuf[wave];
-  const uint32_t k_off = (uint32_t)(qcol * D * 2 + grp * 16);   // byte offset of this lane's K piece
+  unsigned char* kb = kbuf[wave];
   // V copy w puts this lane's 16 bytes at LDS row v_row0 + w*kRowsPerCopy,
   // physical slot v_phys; the swizzle of that row picks the logical slot.
   constexpr int kRowsPerCopy = 1024 / (2 * D);
@@ -546,27 +555,27 @@ __global__ __launch_bounds__(kThreads, 3) void decode_split_balanced(DecodeParam
     for (; u < seg_end; ++u, ++k) {
       const int base = k * kDecodeUnit + wave * 32;
       if (base >= n) continue;                         // this wave's slice is past the length
-      // K into registers (A-operand layout); V straight into this wave's LDS
-      // region by direct copies (copy w lands lane i at byte w*1024 + 16*i).
+      // K then V straight into this wave's LDS regions by direct copies (copy
+      // w lands lane i at byte w*1024 + 16*i): each copy reads whole rows,
+      // 1 KiB contiguous, where loading K into the MFMA operand layout would
+      // touch 16 rows per instruction.  Rows past the length repeat row n-1.
       const uint16_t* kp = kv_row<D>(p.k, p, b, hk, base);   // rows base .. base+31
       const uint16_t* vp = kv_row<D>(p.v, p, b, hk, base);
-      u32x4 kr[2][KS];
       if (base + 32 <= n) {
-        const char* kb = reinterpret_cast<const char*>(kp);
+        const char* kbs = reinterpret_cast<const char*>(kp);
         const char* vbs = reinterpret_cast<const char*>(vp);
 #pragma unroll
-        for (int hlf = 0; hlf < 2; ++hlf)
-#pragma unroll
-          for (int ks = 0; ks < KS; ++ks) kr[hlf][ks] = ld16_stream(kb + k_off + hlf * 16 * D * 2 + ks * 64);
+        for (int w = 0; w < VP; ++w)
+          global_to_lds16_stream(kbs + (v_row0 + w * kRowsPerCopy) * 2 * D + v_slot(w) * 16, kb + w * 1024);
 #pragma unroll
         for (int w = 0; w < VP; ++w)
           global_to_lds16_stream(vbs + (v_row0 + w * kRowsPerCopy) * 2 * D + v_slot(w) * 16, vb + w * 1024);
       } else {
 #pragma unroll
-        for (int hlf = 0; hlf < 2; ++hlf) {
-          const int key = min(base + 16 * hlf + qcol, n - 1) - base;
-#pragma unroll
-          for (int ks = 0; ks < KS; ++ks) kr[hlf][ks] = ld16_stream(kp + key * D + 32 * ks + 8 * grp);
+        for (int w = 0; w < VP; ++w) {
+          const int key = min(base + v_row0 + w * kRowsPerCopy, n - 1) - base;
+          global_to_lds16_stream(reinterpret_cast<const char*>(kp + key * D) + v_slot(w) * 16,
+                          kb + w * 1024);
         }
 #pragma unroll
         for (int w = 0; w < VP; ++w) {
@@ -574,6 +583,19 @@ __global__ __launch_bounds__(kThreads, 3) void decode_split_balanced(DecodeParam
           global_to_lds16_stream(reinterpret_cast<const char*>(vp + key * D) + v_slot(w) * 16,
                           vb + w * 1024);
         }
+      }
+      wait_vmem_below<VP>();   // the K copies have landed (the V copies may be in flight)
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      // K rows into the A-operand layout: lane (qcol, grp) takes row
+      // 16*hlf + qcol, features 32*ks + 8*grp .. +7.
+      u32x4 kr[2][KS];
+#pragma unroll
+      for (int hlf = 0; hlf < 2; ++hlf) {
+        const int r = 16 * hlf + qcol;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+          kr[hlf][ks] = *reinterpret_cast<const u32x4*>(
+              kb + (r * SLOTS + ((4 * ks + grp) ^ (lds_swizzle(r) & (SLOTS - 1)))) * 16);
       }
       f32x4 sacc[2];
 #pragma unroll
