@@ -24,6 +24,7 @@ CASES = [
     (4, 16, 4, 2048, 128, 256, [2048, 1500, 129, 0]),      # query groups, balanced pass
     (2, 8, 1, 512, 64, 128, [512, 300]),                   # d = 64, groups of 8
     (5, 4, 4, 1000, 64, 384, [1000, 999, 385, 384, 17]),   # page size 3 x 128, ragged capacity
+    (3, 4, 2, 768, 64, 128, [768, 200, 1]),                # d = 64, groups of 2, a one-key cache
 ]
 
 

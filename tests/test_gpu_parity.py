@@ -132,6 +132,8 @@ DECODE_CASES = [
     (3, 3, 3, 900, 64, [900, 512, 1]),
     (3, 8, 1, 900, 64, [2, 900, 0]),
     (2, 4, 2, 64, 64, None),
+    (3, 8, 2, 1000, 64, [1000, 0, 383]),
+    (2, 16, 1, 300, 64, [300, 129]),
     # one split per head (capacity <= 512): the split pass writes O itself
     (4, 2, 2, 500, 128, [500, 1, 0, 257]),
     (2, 3, 3, 512, 64, [512, 77]),
