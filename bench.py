@@ -365,7 +365,7 @@ def only(args, torch, attn, wl, dev):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); this build has no "
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); this library has no "
               "multi-GPU path: every workload here runs on a single MI355X.", file=sys.stderr)
         sys.exit(2)
     import torch

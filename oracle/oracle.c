@@ -19,7 +19,7 @@
  * For every (b, h_q, i) row it runs three passes over a materialised score
  * row: (1) scores, (2) max, then exp and sum, then normalise, (3) P V.
  *
- * Readings where the pages are silent (each is listed in the design doc):
+ * Readings where the pages are silent:
  *   - the dot product is multiplied by `scale` first, then the mask is added;
  *   - the mask is additive -inf, so a masked key gets weight exactly 0;
  *   - causal alignment is bottom-right: with len valid keys and S_q queries,
