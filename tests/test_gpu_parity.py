@@ -77,6 +77,13 @@ PREFILL_CASES = [
     (2, 4, 2, 200, 260, 128, True, [260, 100], "f32"),
     (1, 3, 1, 70, 90, 64, False, None, "f32"),
     (1, 2, 2, 1, 33, 128, True, [5], "f32"),
+    # fp32 key groups: many blocks per group, groups with unequal block
+    # counts, an empty sequence; 16-row tiles with a ragged tail at d = 128
+    (2, 2, 2, 100, 700, 64, True, [700, 0], "f32"),
+    (1, 4, 4, 300, 300, 128, False, None, "f32"),
+    # fp32 grids of >= 512 64-row tiles take the 64-row, one-group shape
+    (1, 64, 8, 520, 520, 64, True, None, "f32"),
+    (1, 64, 16, 512, 600, 128, True, [600], "f32"),
 ]
 
 
