@@ -9,8 +9,8 @@
 //
 // Mapping: 512 threads per workgroup, eight adjacent lanes per query row,
 // each lane owning an eighth of the features.  A score is eight partial dot
-// products (one per lane) added by three exchanges, so every lane of the row
-// holds the full score; P V then accumulates each lane's eighth of the
+// products (one per lane) added by three DPP lane moves, so every lane of
+// the row holds the full score; P V then accumulates each lane's eighth of the
 // output.  This path is bound by each lane's serial chain over the keys, not
 // by bandwidth, and has two tile shapes:
 //   - small grids: 8-row tiles, the eight waves forming eight key groups;
@@ -40,6 +40,25 @@ constexpr int kF32Threads = 512;                      // 64 rows' worth of lanes
 // which put eight times the workgroups on the chip and split each row's keys
 // eight ways.
 constexpr int64_t kF32LargeGrid = 512;
+
+// Lane move within each row of 16 lanes (DPP control CTRL), as a float.
+template <int CTRL>
+__device__ __forceinline__ float dpp_move(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+
+// Sum over the 8 adjacent lanes of a query row (an aligned half-row) with
+// DPP moves: swap neighbours (quad_perm 1,0,3,2), swap pairs (quad_perm
+// 2,3,0,1), then mirror the half-row (lane i with 7 - i, in the other quad).
+// Every lane ends with ((a0+a1)+(a2+a3)) + ((a4+a5)+(a6+a7)) up to the
+// order of each addition's operands: the sum a butterfly over lane masks 1,
+// 2, 4 forms, without going through the LDS crossbar.
+__device__ __forceinline__ float row8_sum(float a) {
+  a += dpp_move<0xB1>(a);
+  a += dpp_move<0x4E>(a);
+  a += dpp_move<0x141>(a);
+  return a;
+}
 
 template <int D, bool CAUSAL, int ROWS>
 __global__ __launch_bounds__(kF32Threads) void prefill_f32_kernel(PrefillParams p) {
@@ -120,9 +139,7 @@ __global__ __launch_bounds__(kF32Threads) void prefill_f32_kernel(PrefillParams 
         a = fmaf(q[c + 2], kv[2], a);
         a = fmaf(q[c + 3], kv[3], a);
       }
-#pragma unroll
-      for (int msk = 1; msk < kF32Parts; msk <<= 1) a += shfl_xor(a, msk);   // the row's lanes are adjacent
-      s[rr] = a;
+      s[rr] = row8_sum(a);   // the row's 8 lanes are adjacent and aligned
     }
     float mt = kNegInf;
 #pragma unroll
