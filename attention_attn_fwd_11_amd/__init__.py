@@ -4,8 +4,8 @@ Thin ctypes layer over the C ABI in include/attn.h.  The functions named
 attn_* take raw device pointers and sizes and return the C status code,
 exactly like their C counterparts.  `prefill()` and `decode()` marshal torch
 tensors onto those calls: they check shapes, dtypes and devices, allocate the
-output, pass torch's current HIP stream and keep a per-device decode
-workspace.  Every step of the computation runs in the HIP kernels; there is
+output, pass torch's current HIP stream and keep a decode workspace per
+(device, stream).  Every step of the computation runs in the HIP kernels; there is
 no fallback path: the library is loaded on first use, and every entry point
 raises ImportError if libattn.so has not been built.
 """
@@ -259,14 +259,54 @@ def prefill_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen
     return o
 
 
-def workspace_for(device, nbytes):
-    """Per-device scratch buffer of at least nbytes (grown on demand)."""
-    key = torch.device(device).index
+def workspace_for(device, nbytes, stream=None):
+    """Cached decode scratch buffer of at least nbytes for (device, stream).
+
+    Calls that share a workspace must be ordered on one stream, so the cache
+    keeps one buffer per (device, stream): decodes issued on different
+    streams never share partials.  The buffer is allocated while its stream
+    is current, so when it grows the caching allocator reuses the old memory
+    only after the work already queued on that stream.  Under graph capture
+    a cached buffer could be regrown (and freed) after the graph has baked
+    in its address, so there the caller must pass `workspace=` and keep it
+    alive as long as the graph.
+    """
+    dev = torch.device(device)
+    if torch.cuda.is_current_stream_capturing():
+        raise RuntimeError("decode under graph capture needs an explicit workspace= tensor that "
+                           "outlives the graph (see attn_decode_workspace_bytes)")
+    if stream is None:
+        stream = torch.cuda.current_stream(dev)
+    key = (dev.index, stream.cuda_stream)
     ws = _workspaces.get(key)
     if ws is None or ws.numel() < nbytes:
-        ws = torch.empty(max(nbytes, 1 << 20), dtype=torch.uint8, device=device)
+        with torch.cuda.stream(stream):
+            ws = torch.empty(max(nbytes, 1 << 20), dtype=torch.uint8, device=dev)
         _workspaces[key] = ws
     return ws
+
+
+def _decode_buffers(q, o, ws, need, others):
+    """Checks shared by the decode wrappers: out has q's shape, dtype and
+    device; the cache tensors and the workspace sit on q's device; the
+    workspace is large enough.  Returns (o, ws)."""
+    for name, t in others:
+        if t.device != q.device:
+            raise ValueError(f"{name} must be on q's device ({q.device}), got {t.device}")
+    if o is None:
+        o = torch.empty_like(q)
+    _check_tensor("out", o, torch.bfloat16)
+    if o.shape != q.shape or o.device != q.device:
+        raise ValueError("out must have q's shape and device")
+    if ws is None:
+        ws = workspace_for(q.device, need)
+    else:
+        if not isinstance(ws, torch.Tensor) or ws.device != q.device or not ws.is_contiguous():
+            raise ValueError("workspace must be a contiguous tensor on q's device")
+        if ws.numel() * ws.element_size() < need:
+            raise ValueError(f"workspace holds {ws.numel() * ws.element_size()} bytes, "
+                             f"{need} needed")
+    return o, ws
 
 
 def decode(q, k_cache, v_cache, kv_lens=None, scale=None, out=None, workspace=None):
@@ -274,7 +314,8 @@ def decode(q, k_cache, v_cache, kv_lens=None, scale=None, out=None, workspace=No
     (bf16); kv_lens int32 [B] on the device (None: every row is valid).
 
     Returns o [B,H_q,1,d] bf16.  Runs the split and combine kernels on torch's
-    current stream; the workspace (if not given) is cached per device.
+    current stream; the workspace (if not given) is cached per (device,
+    stream), and must be given under graph capture.
     """
     for name, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache)):
         _check_tensor(name, t, torch.bfloat16)
@@ -287,9 +328,9 @@ def decode(q, k_cache, v_cache, kv_lens=None, scale=None, out=None, workspace=No
     lens = _lens(kv_lens, B, q.device)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    o = out if out is not None else torch.empty_like(q)
     need = attn_decode_workspace_bytes(B, H_q, H_kv, S_kv, d)
-    ws = workspace if workspace is not None else workspace_for(q.device, need)
+    o, ws = _decode_buffers(q, out, workspace, need,
+                            (("k_cache", k_cache), ("v_cache", v_cache)))
     stream = torch.cuda.current_stream(q.device).cuda_stream
     st = attn_decode_fwd(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(o), B, H_q, H_kv, S_q, S_kv,
                          d, 0, float(scale), _ptr(lens), ATTN_BF16, _ptr(ws),
@@ -306,7 +347,8 @@ def decode_paged(q, k_pages, v_pages, block_table, kv_lens=None, scale=None, out
     (page of each sequence's page_size-key block); kv_lens int32 [B] or None.
 
     Returns o [B,H_q,1,d] bf16, on torch's current stream; the workspace (if
-    not given) is cached per device.
+    not given) is cached per (device, stream), and must be given under graph
+    capture.
     """
     for name, t in (("q", q), ("k_pages", k_pages), ("v_pages", v_pages)):
         _check_tensor(name, t, torch.bfloat16)
@@ -323,9 +365,9 @@ def decode_paged(q, k_pages, v_pages, block_table, kv_lens=None, scale=None, out
     lens = _lens(kv_lens, B, q.device)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    o = out if out is not None else torch.empty_like(q)
     need = attn_decode_workspace_bytes(B, H_q, H_kv, max_blocks * page_size, d)
-    ws = workspace if workspace is not None else workspace_for(q.device, need)
+    o, ws = _decode_buffers(q, out, workspace, need,
+                            (("k_pages", k_pages), ("v_pages", v_pages)))
     stream = torch.cuda.current_stream(q.device).cuda_stream
     st = attn_decode_paged_fwd(_ptr(q), _ptr(k_pages), _ptr(v_pages), _ptr(o), B, H_q, H_kv, d,
                                float(scale), _ptr(block_table), max_blocks, page_size, num_pages,

@@ -4,17 +4,16 @@ This module only describes shapes and draws random numbers; it holds none of
 the attention arithmetic, so both the GPU path and the CPU oracle can be fed
 from it.
 
-Recipe (the same for every workload):
-  1. if the workload has ragged KV lengths, draw them first, on a CPU
-     torch.Generator seeded with `seed`: integers uniform on [lo, hi], both
-     ends included;
-  2. on a torch.Generator of the target device seeded with `seed`, draw Q,
-     then K, then V as float32 standard normals (`torch.randn`);
+Recipe (the same for every workload), all on one CPU torch.Generator
+seeded with `seed`:
+  1. if the workload has ragged KV lengths, draw them first: integers
+     uniform on [lo, hi], both ends included;
+  2. draw Q, then K, then V as float32 standard normals (`torch.randn`);
   3. multiply K by the workload's `k_mult` (a power of two, so exact);
-  4. cast to the workload dtype (bf16 by round-to-nearest-even).
-Values therefore depend on the device the generator runs on; every check
-compares the GPU output against the oracle evaluated on the very tensors the
-GPU received.
+  4. cast to the workload dtype (bf16 by round-to-nearest-even);
+  5. copy the result to the target device.
+The values do not depend on the device, so the oracle can be evaluated on
+the CPU tensors drawn here.
 """
 from dataclasses import dataclass, field
 import math
@@ -83,33 +82,35 @@ WORKLOADS = [
 BY_NAME = {w.name: w for w in WORKLOADS}
 
 
-def kv_lengths(w, seed=0):
-    """Per-sequence KV lengths (int32, CPU) for workload w."""
+def _lengths(w, g):
     if w.len_range is None:
         return torch.full((w.B,), w.Skv, dtype=torch.int32)
-    g = torch.Generator(device="cpu").manual_seed(seed)
     lo, hi = w.len_range
     return torch.randint(lo, hi + 1, (w.B,), generator=g, dtype=torch.int64).to(torch.int32)
 
 
+def kv_lengths(w, seed=0):
+    """Per-sequence KV lengths (int32, CPU) for workload w: the first draw of
+    the recipe."""
+    return _lengths(w, torch.Generator(device="cpu").manual_seed(seed))
+
+
 def generate(w, device="cpu", seed=0):
-    """Seeded inputs for workload w on `device`.
+    """Seeded inputs for workload w, drawn on the CPU and copied to `device`.
 
     Returns dict(q, k, v, kv_lens) with q [B,Hq,Sq,d], k/v [B,Hkv,Skv,d] in the
     workload dtype and kv_lens int32 [B] (on `device`).
     """
-    lens = kv_lengths(w, seed)
-    dev = torch.device(device)
-    g = torch.Generator(device=dev).manual_seed(seed)
-    q = torch.randn((w.B, w.Hq, w.Sq, w.d), generator=g, device=dev, dtype=torch.float32)
-    q = q.to(w.torch_dtype)
-    k = torch.randn((w.B, w.Hkv, w.Skv, w.d), generator=g, device=dev, dtype=torch.float32)
+    g = torch.Generator(device="cpu").manual_seed(seed)
+    lens = _lengths(w, g)
+    q = torch.randn((w.B, w.Hq, w.Sq, w.d), generator=g, dtype=torch.float32).to(w.torch_dtype)
+    k = torch.randn((w.B, w.Hkv, w.Skv, w.d), generator=g, dtype=torch.float32)
     if w.k_mult != 1.0:
         k.mul_(w.k_mult)
     k = k.to(w.torch_dtype)
-    v = torch.randn((w.B, w.Hkv, w.Skv, w.d), generator=g, device=dev, dtype=torch.float32)
-    v = v.to(w.torch_dtype)
-    return {"q": q, "k": k, "v": v, "kv_lens": lens.to(dev)}
+    v = torch.randn((w.B, w.Hkv, w.Skv, w.d), generator=g, dtype=torch.float32).to(w.torch_dtype)
+    dev = torch.device(device)
+    return {"q": q.to(dev), "k": k.to(dev), "v": v.to(dev), "kv_lens": lens.to(dev)}
 
 
 def random_problem(B, Hq, Hkv, Sq, Skv, d, dtype="bf16", device="cpu", seed=0, k_mult=1.0,
@@ -186,15 +187,15 @@ def paged_cache(k, v, kv_lens, page_size, seed=0, spare_pages=3, fill=float("nan
 
 def varlen_problem(q_lens, k_lens, Hq, Hkv, d, device="cpu", seed=0):
     """Packed sequences by the same recipe (Q, then K, then V as float32
-    normals on a generator of `device` seeded with `seed`, cast to bf16):
-    q [sum(q_lens), Hq, d], k and v [sum(k_lens), Hkv, d], and the int32
-    offsets cu_q, cu_k [B+1] on `device`."""
+    normals on a CPU generator seeded with `seed`, cast to bf16, copied to
+    `device`): q [sum(q_lens), Hq, d], k and v [sum(k_lens), Hkv, d], and the
+    int32 offsets cu_q, cu_k [B+1] on `device`."""
     dev = torch.device(device)
-    g = torch.Generator(device=dev).manual_seed(seed)
+    g = torch.Generator(device="cpu").manual_seed(seed)
     tq, tk = int(sum(q_lens)), int(sum(k_lens))
-    q = torch.randn((tq, Hq, d), generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
-    k = torch.randn((tk, Hkv, d), generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
-    v = torch.randn((tk, Hkv, d), generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
+    q = torch.randn((tq, Hq, d), generator=g, dtype=torch.float32).to(torch.bfloat16).to(dev)
+    k = torch.randn((tk, Hkv, d), generator=g, dtype=torch.float32).to(torch.bfloat16).to(dev)
+    v = torch.randn((tk, Hkv, d), generator=g, dtype=torch.float32).to(torch.bfloat16).to(dev)
     cu_q = torch.tensor([0] + list(torch.tensor(q_lens).cumsum(0).tolist()), dtype=torch.int32,
                         device=dev)
     cu_k = torch.tensor([0] + list(torch.tensor(k_lens).cumsum(0).tolist()), dtype=torch.int32,

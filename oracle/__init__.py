@@ -5,7 +5,9 @@ import this package.  The product library neither imports nor links it, and
 the two share no code.
 
 `attention()` and `attention_rows()` call the fp64 three-pass definition in
-oracle.c (standard attention as set out in "GPU learning day 24: Operator
+oracle.c (or, given lib=oracle.rowblock, the same definition evaluated one
+block of query rows at a time with fp64 library matrix products, fast enough
+for whole outputs of the large workloads) (standard attention as set out in "GPU learning day 24: Operator
 Fusion", section 3.4, with the two-pass softmax of "Optimizing Decoder
 Attention for LLMs on GPU", traditional-approach step 3).  `decode()` is the
 same definition with one query row per head, as in the decoding setting of
@@ -106,8 +108,15 @@ def _shapes(q, k, v):
     return B, Hq, Hkv, Sq, Skv, d
 
 
+def _rowblock(lib):
+    return getattr(lib, "IS_ROWBLOCK", False)
+
+
 def attention(q, k, v, causal, scale, kv_lens=None, want_lse=False, want_p=False, lib=None):
     """Full fp64 attention.  Returns o [B,H_q,S_q,d] (and lse, p if asked)."""
+    if _rowblock(lib):
+        return lib.attention(q, k, v, causal, scale, kv_lens=kv_lens, want_lse=want_lse,
+                             want_p=want_p)
     qa, dt = _as_stored(q)
     ka, dtk = _as_stored(k)
     va, dtv = _as_stored(v)
@@ -133,6 +142,8 @@ def attention(q, k, v, causal, scale, kv_lens=None, want_lse=False, want_p=False
 
 def attention_rows(q, k, v, causal, scale, rows, kv_lens=None, want_lse=False, lib=None):
     """fp64 attention for selected (b, h_q, i) rows.  Returns o [n, d] (and lse [n])."""
+    if _rowblock(lib):
+        return lib.attention_rows(q, k, v, causal, scale, rows, kv_lens=kv_lens, want_lse=want_lse)
     qa, dt = _as_stored(q)
     ka, dtk = _as_stored(k)
     va, dtv = _as_stored(v)

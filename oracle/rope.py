@@ -57,9 +57,10 @@ def positions(S_q, n):
     return qpos, np.arange(n, dtype=np.int64)
 
 
-def attention_rope(q, k, v, causal, scale, table, kv_lens=None):
+def attention_rope(q, k, v, causal, scale, table, kv_lens=None, lib=None):
     """fp64 attention of rope(q), rope(k), v over [B, H, S, d] inputs, with
-    per-batch positions as above (kv_lens as in the oracle's attention)."""
+    per-batch positions as above (kv_lens as in the oracle's attention; lib
+    selects the evaluation as there)."""
     qf, kf = _f64(q), _f64(k)
     B, Hq, Sq, d = qf.shape
     Skv = kf.shape[2]
@@ -70,4 +71,4 @@ def attention_rope(q, k, v, causal, scale, table, kv_lens=None):
         qpos, _ = positions(Sq, lens[b])
         qr[b] = rope(qf[b], table, qpos)
         kr[b] = rope(kf[b], table, np.arange(Skv, dtype=np.int64))
-    return _attention(qr, kr, _f64(v), causal, scale, kv_lens=kv_lens)
+    return _attention(qr, kr, _f64(v), causal, scale, kv_lens=kv_lens, lib=lib)

@@ -195,3 +195,14 @@ def test_workspace_balanced_query_groups(lib, monkeypatch):
     assert ws >= 2 * 8 * 8 * 129 * 4
     monkeypatch.setenv("ATTN_DECODE_CHUNK", "4096")     # no effect on the balanced pass
     assert attn.attn_decode_workspace_bytes(2, 8, 2, 1000, 128) == ws
+
+
+def test_cached_workspace_refused_under_graph_capture(monkeypatch):
+    """A graph captured with the cached decode workspace would keep its
+    address after a later, larger call regrows (frees) it, so under capture
+    the wrapper demands an explicit workspace (checked before any HIP call)."""
+    import torch
+    import attention_attn_fwd_11_amd as attn
+    monkeypatch.setattr(torch.cuda, "is_current_stream_capturing", lambda: True)
+    with pytest.raises(RuntimeError, match="workspace"):
+        attn.workspace_for("cuda:0", 1024)
