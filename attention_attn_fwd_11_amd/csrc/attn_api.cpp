@@ -111,13 +111,34 @@ int device_cus(int* dev_out) {
 
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
+// Partial rows (one per split and query head, or per run and query head on
+// the balanced pass) a decode of this shape may write.
+size_t partial_rows(int32_t B, int32_t H_q, int32_t H_kv, int32_t S_kv) {
+  const int chunk = decode_chunk(B, H_q, H_kv, S_kv);
+  const int64_t n_split = (S_kv + chunk - 1) / chunk;
+  if (decode_balanced(B, H_q, H_kv)) {
+    // a run per (head, workgroup range) boundary: fewer than B*H_kv + n_wg,
+    // with n_wg at most kDecodeMaxWg and at most the number of units
+    int64_t wg = (int64_t)B * H_kv * n_split;
+    if (wg > attn::kDecodeMaxWg) wg = attn::kDecodeMaxWg;
+    return (size_t)((int64_t)B * H_kv + wg) * (H_q / H_kv);
+  }
+  return (size_t)B * H_q * n_split;
+}
+
 size_t workspace_bytes(int32_t B, int32_t H_q, int32_t H_kv, int32_t S_kv, int32_t d) {
   if (B <= 0 || S_kv <= 0 || H_q < 1 || H_kv < 1 || H_q % H_kv != 0 || (d != 64 && d != 128))
     return 0;
-  const int chunk = decode_chunk(B, H_q, H_kv, S_kv);
-  const int64_t n_split = (S_kv + chunk - 1) / chunk;
-  const size_t rows = (size_t)B * H_q * n_split;
+  const size_t rows = partial_rows(B, H_q, H_kv, S_kv);
   return round_up(rows * d * sizeof(float), 256) + round_up(rows * sizeof(float), 256);
+}
+
+// What the decode kernels implement: bf16, d 64 or 128, query groups of
+// 1, 2, 4, 8 or 16 heads.
+bool decode_supported(int32_t H_q, int32_t H_kv, int32_t d, attn_dtype_t dtype) {
+  const int G = H_q / H_kv;
+  return dtype == ATTN_BF16 && (d == 64 || d == 128) &&
+         (G == 1 || G == 2 || G == 4 || G == 8 || G == 16);
 }
 
 // Decode after the entry point's own checks (shared by the contiguous and the
@@ -127,10 +148,7 @@ attn_status_t run_decode(const void* q, const void* k, const void* v, void* o, i
                          attn_dtype_t dtype, void* workspace, size_t ws_bytes, void* stream,
                          const int32_t* block_table, int32_t max_blocks, int32_t page_size,
                          int32_t num_pages) {
-  if (dtype != ATTN_BF16) return ATTN_ERR_UNSUPPORTED;
-  if (d != 64 && d != 128) return ATTN_ERR_UNSUPPORTED;
-  const int G = H_q / H_kv;
-  if (G != 1 && G != 2 && G != 4 && G != 8 && G != 16) return ATTN_ERR_UNSUPPORTED;
+  if (!decode_supported(H_q, H_kv, d, dtype)) return ATTN_ERR_UNSUPPORTED;
   if (B == 0) return ATTN_OK;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (S_kv == 0) {
@@ -165,9 +183,10 @@ attn_status_t run_decode(const void* q, const void* k, const void* v, void* o, i
     }
     const int64_t max_units = (int64_t)B * H_kv * p.n_split;
     if (wg > max_units) wg = max_units;
+    if (wg > attn::kDecodeMaxWg) wg = attn::kDecodeMaxWg;
     p.n_wg = (int)wg;
   }
-  const size_t rows = (size_t)B * H_q * p.n_split;
+  const size_t rows = partial_rows(B, H_q, H_kv, S_kv);
   p.part_o = static_cast<float*>(workspace);
   p.part_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) +
                                         round_up(rows * d * sizeof(float), 256));

@@ -435,10 +435,17 @@ __global__ __launch_bounds__(kThreads, 3) void decode_split_mfma(DecodeParams p)
 // recomputes their prefix sum in LDS.  Workgroup w takes units
 // [w*R, (w+1)*R), R = ceil(U / gridDim.x), walking across heads: runs of units
 // of one head are merged on the fly, and each run ("segment") leaves one
-// partial (o, base-2 lse) per query head, stored at the slot of the
-// segment's first unit.  The combine kernel finds a head's segments from the
-// same prefix sums and R.
+// partial (o, base-2 lse) per query head, at the slot run_slot() gives it
+// (fewer than B * H_kv + gridDim.x slots in all, whatever the lengths).  The
+// combine kernel finds a head's segments from the same prefix sums and R.
 // ---------------------------------------------------------------------------
+
+// Partial slot of the run that starts at unit u of flattened head h = b *
+// H_kv + g, with R units per workgroup.  A run starts at its head's first unit
+// or at a multiple of R, so runs of one head have distinct u / R, and a later
+// head's runs start at units no smaller than an earlier head's: h + u / R is
+// distinct for every run and below B * H_kv + (number of workgroups).
+__device__ __forceinline__ int run_slot(int h, int u, int R) { return h + u / R; }
 
 // Exclusive prefix over batches of H_kv * ceil(n_b / kDecodeUnit) into pre[0..B]
 // (pre[B] = total units).  All threads of the workgroup take part.
@@ -679,7 +686,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_balanced(DecodeParam
         L += wt * mrg_l[w][qi];
         acc += wt * mrg_o[w][qi][d];
       }
-      const int64_t slot = (int64_t)seg_start * G + qi;
+      const int64_t slot = (int64_t)run_slot(b * p.Hkv + hk, seg_start, R) * G + qi;
       p.part_o[slot * D + d] = acc / L;
       if (d == 0) p.part_lse[slot] = M + log2_fast(L);
     }
@@ -727,10 +734,12 @@ __global__ __launch_bounds__(64) void decode_combine_balanced(DecodeParams p) {
 #pragma unroll
   for (int e = 0; e < PER; ++e) acc[e] = 0.f;
   float M = kNegInf;
-  for (int s = hs; s < he; s = (s / R + 1) * R) M = fmaxf(M, p.part_lse[(int64_t)s * G + qi]);
+  const int head = b * p.Hkv + g;
+  for (int s = hs; s < he; s = (s / R + 1) * R)
+    M = fmaxf(M, p.part_lse[(int64_t)run_slot(head, s, R) * G + qi]);
   float Wsum = 0.f;
   for (int s = hs; s < he; s = (s / R + 1) * R) {
-    const int64_t slot = (int64_t)s * G + qi;
+    const int64_t slot = (int64_t)run_slot(head, s, R) * G + qi;
     const float wt = exp2_fast(p.part_lse[slot] - M);
     Wsum += wt;
 #pragma unroll

@@ -45,8 +45,10 @@ struct DecodeParams {
   const void* v;
   void* o;
   const int32_t* kv_lens;  // device int32[B] or nullptr
-  float* part_o;           // [B, Hq, n_split, d] fp32
-  float* part_lse;         // [B, Hq, n_split]   fp32, base-2 log-sum-exp
+  // Chunked pass: [B, Hq, n_split, d] and [B, Hq, n_split]; balanced pass:
+  // [B * Hkv + n_wg, G, d] and [B * Hkv + n_wg, G] (one slot per run).
+  float* part_o;           // fp32 partial outputs, normalised
+  float* part_lse;         // fp32 base-2 log-sum-exps
   int B, Hq, Hkv, Skv, d;
   int chunk;               // keys per split (G = 1) or per unit (G >= 2)
   int n_split;             // partial slots per (batch, query head)
@@ -65,6 +67,9 @@ struct DecodeParams {
 constexpr int kDecodeMaxBatch = 2048;
 // Keys per work unit of the balanced decode pass (4 waves x 32 keys).
 constexpr int kDecodeUnit = 128;
+// Most workgroups of the balanced decode pass; its partials need at most
+// B * H_kv + (workgroups) slots per query head of a group.
+constexpr int kDecodeMaxWg = 1024;
 
 hipError_t launch_prefill_f32(const PrefillParams& p, hipStream_t stream);
 hipError_t launch_prefill_bf16(const PrefillParams& p, hipStream_t stream);

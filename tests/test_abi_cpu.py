@@ -190,9 +190,14 @@ def test_workspace_follows_chunk_override(lib, monkeypatch):
 
 
 def test_workspace_balanced_query_groups(lib, monkeypatch):
-    # query groups use 128-key units: one partial slot per unit and query head
+    # query groups use 128-key units spread over at most 1024 workgroups: a
+    # partial per run and query head, fewer than B*H_kv + workgroups runs
+    # (here 2*2 heads of 8 units: at most 4 + 32 runs of 4 query heads)
     ws = attn.attn_decode_workspace_bytes(2, 8, 2, 1000, 128)
-    assert ws >= 2 * 8 * 8 * 129 * 4
+    assert ws >= (2 * 2 + 32) * 4 * 129 * 4
+    # the bound does not grow with the cache capacity past 1024 workgroups
+    big = attn.attn_decode_workspace_bytes(128, 32, 8, 8192, 128)
+    assert big >= (128 * 8 + 1024) * 4 * 129 * 4 and big < 8 << 20
     monkeypatch.setenv("ATTN_DECODE_CHUNK", "4096")     # no effect on the balanced pass
     assert attn.attn_decode_workspace_bytes(2, 8, 2, 1000, 128) == ws
 
