@@ -18,7 +18,8 @@ import torch
 
 __all__ = [
     "ATTN_F32", "ATTN_BF16", "AttnError", "attn_prefill_fwd", "attn_decode_fwd",
-    "attn_decode_paged_fwd", "attn_prefill_varlen_fwd", "attn_prefill_rope_fwd",
+    "attn_decode_paged_fwd", "attn_decode_noalloc_fwd", "ATTN_DECODE_NOALLOC_SCRATCH_BYTES",
+    "attn_prefill_varlen_fwd", "attn_prefill_rope_fwd",
     "attn_prefill_rope_workspace_bytes", "attn_decode_workspace_bytes",
     "attn_status_str", "attn_last_hip_error", "prefill", "prefill_varlen", "decode",
     "decode_paged", "library_path",
@@ -64,6 +65,9 @@ def _load():
         lib.attn_prefill_rope_workspace_bytes.argtypes = [i32, i32, i32, i32]
         lib.attn_prefill_rope_workspace_bytes.restype = ctypes.c_size_t
         lib.attn_prefill_rope_fwd.restype = ctypes.c_int
+        lib.attn_decode_noalloc_fwd.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32,
+                                                f32, vp, ctypes.c_int, vp]
+        lib.attn_decode_noalloc_fwd.restype = ctypes.c_int
         lib.attn_decode_paged_fwd.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, f32, vp, i32, i32,
                                               i32, vp, ctypes.c_int, vp, sz, vp]
         lib.attn_decode_paged_fwd.restype = ctypes.c_int
@@ -107,6 +111,16 @@ def attn_decode_fwd(q, k_cache, v_cache, o, B, H_q, H_kv, S_q, S_kv, d, causal, 
                     dtype, workspace, workspace_bytes, stream):
     return _load().attn_decode_fwd(q, k_cache, v_cache, o, B, H_q, H_kv, S_q, S_kv, d, causal,
                                    scale, kv_lens, dtype, workspace, workspace_bytes, stream)
+
+
+def attn_decode_noalloc_fwd(q, k_cache, v_cache, o, B, H_q, H_kv, S_q, S_kv, d, causal, scale,
+                            kv_lens, dtype, stream):
+    return _load().attn_decode_noalloc_fwd(q, k_cache, v_cache, o, B, H_q, H_kv, S_q, S_kv, d,
+                                           causal, scale, kv_lens, dtype, stream)
+
+
+# Size of the static scratch behind attn_decode_noalloc_fwd (include/attn.h).
+ATTN_DECODE_NOALLOC_SCRATCH_BYTES = 32 << 20
 
 
 def attn_decode_paged_fwd(q, k_pages, v_pages, o, B, H_q, H_kv, d, scale, block_table, max_blocks,

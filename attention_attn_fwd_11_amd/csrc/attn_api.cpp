@@ -141,6 +141,45 @@ bool decode_supported(int32_t H_q, int32_t H_kv, int32_t d, attn_dtype_t dtype) 
          (G == 1 || G == 2 || G == 4 || G == 8 || G == 16);
 }
 
+// Scratch of the allocation-free decode entry point (attn_decode_noalloc_fwd):
+// one copy per GPU the library runs on, held until the process ends.  Host
+// code never passes `scratch` itself (in host code its name stands for a host
+// shadow, not a device address); it uses the address static_scratch() looked
+// up with hipGetSymbolAddress for the device the work runs on.
+constexpr size_t kScratchBytes = ATTN_DECODE_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+// Device address of `scratch` on the device of `stream` (the current device
+// for the null stream), looked up once per device with that device current.
+attn_status_t static_scratch(hipStream_t stream, void** out) {
+  static std::mutex mu;
+  static void* addr[64] = {};
+  int cur = 0, dev = 0;
+  hipError_t e = hipGetDevice(&cur);
+  if (e != hipSuccess) return hip_fail("hipGetDevice", e);
+  dev = cur;
+  if (stream) {
+    e = hipStreamGetDevice(stream, &dev);
+    if (e != hipSuccess) return hip_fail("hipStreamGetDevice", e);
+  }
+  if (dev < 0 || dev >= 64) return hip_fail("device index out of range", hipErrorInvalidDevice);
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    if (dev != cur && (e = hipSetDevice(dev)) != hipSuccess) return hip_fail("hipSetDevice", e);
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (dev != cur) {
+      const hipError_t r = hipSetDevice(cur);
+      if (e == hipSuccess && r != hipSuccess) e = r;
+    }
+    if (e != hipSuccess) return hip_fail("hipGetSymbolAddress(scratch)", e);
+    if (!ptr) return hip_fail("hipGetSymbolAddress(scratch)", hipErrorInvalidSymbol);
+    addr[dev] = ptr;
+  }
+  *out = addr[dev];
+  return ATTN_OK;
+}
+
 // Decode after the entry point's own checks (shared by the contiguous and the
 // paged cache; block_table == nullptr selects the contiguous layout).
 attn_status_t run_decode(const void* q, const void* k, const void* v, void* o, int32_t B, int32_t H_q,
@@ -351,6 +390,27 @@ attn_status_t attn_decode_fwd(const void* q, const void* k_cache, const void* v_
   if (S_q != 1) return ATTN_ERR_SHAPE;
   return run_decode(q, k_cache, v_cache, o, B, H_q, H_kv, S_kv, d, scale, kv_lens, dtype, workspace,
                     workspace_bytes, stream, nullptr, 0, 0, 0);
+}
+
+attn_status_t attn_decode_noalloc_fwd(const void* q, const void* k_cache, const void* v_cache,
+                                      void* o, int32_t B, int32_t H_q, int32_t H_kv, int32_t S_q,
+                                      int32_t S_kv, int32_t d, int32_t causal, float scale,
+                                      const int32_t* kv_lens, attn_dtype_t dtype, void* stream) {
+  g_hip_error[0] = '\0';
+  attn_status_t st = check_common(q, k_cache, v_cache, o, B, H_q, H_kv, S_q, S_kv, d, causal,
+                                  scale, dtype);
+  if (st != ATTN_OK) return st;
+  if (S_q != 1) return ATTN_ERR_SHAPE;
+  if (!decode_supported(H_q, H_kv, d, dtype)) return ATTN_ERR_UNSUPPORTED;
+  const size_t need = workspace_bytes(B, H_q, H_kv, S_kv, d);
+  if (need > kScratchBytes) return ATTN_ERR_WORKSPACE;   // beyond the static scratch
+  void* ws = nullptr;
+  if (need > 0) {
+    st = static_scratch(static_cast<hipStream_t>(stream), &ws);
+    if (st != ATTN_OK) return st;
+  }
+  return run_decode(q, k_cache, v_cache, o, B, H_q, H_kv, S_kv, d, scale, kv_lens, dtype, ws,
+                    kScratchBytes, stream, nullptr, 0, 0, 0);
 }
 
 attn_status_t attn_decode_paged_fwd(const void* q, const void* k_pages, const void* v_pages, void* o,

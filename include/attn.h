@@ -24,8 +24,8 @@
  *     bottom right: query i sees key j iff j <= i + n_b - S_q.  A row that sees
  *     no key is written as 0.
  *   - Pointers: device pointers, 16-byte aligned.  Buffers are owned by the
- *     caller; the library allocates nothing, keeps no pointer after a call
- *     returns, and only enqueues work on `stream` (a hipStream_t; NULL means
+ *     caller; the library allocates nothing (attn_decode_noalloc_fwd uses a
+ *     static array of its own), keeps no pointer after a call returns, and only enqueues work on `stream` (a hipStream_t; NULL means
  *     the null stream).  The caller keeps buffers alive until the stream has
  *     run the work.  A pointer may be NULL only when its tensor has no
  *     elements.
@@ -37,8 +37,10 @@
  *     error nothing is launched and O is untouched.  ATTN_ERR_HIP means a HIP
  *     call failed; attn_last_hip_error() then names it.
  *   - Thread safety: the library is stateless apart from a per-device cache
- *     of the compute-unit count (filled once) and a thread-local error string.
- *     Concurrent calls on different streams are safe.
+ *     of the compute-unit count (filled once), a thread-local error string
+ *     and the static scratch of attn_decode_noalloc_fwd (see there).
+ *     Concurrent calls on different streams are safe, except that
+ *     allocation-free decodes on one GPU share its scratch.
  */
 #ifndef ATTN_H
 #define ATTN_H
@@ -190,6 +192,34 @@ attn_status_t attn_decode_fwd(const void* q, const void* k_cache, const void* v_
  * invalid or the problem is empty).  Pure host function; no HIP call.
  */
 size_t attn_decode_workspace_bytes(int32_t B, int32_t H_q, int32_t H_kv, int32_t S_kv, int32_t d);
+
+/*
+ * Allocation-free single-query decode, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).
+ *
+ * Arguments and results exactly as attn_decode_fwd, without the workspace:
+ * the split partials go to a static device array of
+ * ATTN_DECODE_NOALLOC_SCRATCH_BYTES bytes inside the library (one per GPU,
+ * reserved when the library's code is loaded on that GPU and held until the
+ * process ends).  A call whose attn_decode_workspace_bytes(B, H_q, H_kv, S_kv,
+ * d) exceeds that size returns ATTN_ERR_WORKSPACE and launches nothing.  The
+ * call allocates nothing (no hipMalloc, no hipFree); the first call on a GPU
+ * looks up the array's device address once (hipGetSymbolAddress).  The
+ * kernels are attn_decode_fwd's, so O is bitwise the same.
+ *
+ * Every call on one GPU shares that GPU's array, which keeps the last call's
+ * contents (nothing in it needs to start at zero).  Two calls that overlap
+ * on one GPU -- on different streams, or on one stream inside graphs that
+ * run concurrently -- race on it: order them on one stream.  The stream must
+ * belong to a device whose copy of the library's code is loaded (any device
+ * the process can use).
+ */
+#define ATTN_DECODE_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+attn_status_t attn_decode_noalloc_fwd(const void* q, const void* k_cache, const void* v_cache,
+                                      void* o, int32_t B, int32_t H_q, int32_t H_kv, int32_t S_q,
+                                      int32_t S_kv, int32_t d, int32_t causal, float scale,
+                                      const int32_t* kv_lens, attn_dtype_t dtype, void* stream);
 
 /*
  * Single-query decode over a paged KV cache.

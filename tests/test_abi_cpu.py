@@ -35,7 +35,7 @@ def test_exports_every_declared_symbol(lib):
     names = declared_functions()
     assert {"attn_prefill_fwd", "attn_prefill_rope_fwd", "attn_prefill_rope_workspace_bytes",
             "attn_prefill_varlen_fwd", "attn_decode_fwd",
-            "attn_decode_paged_fwd",
+            "attn_decode_paged_fwd", "attn_decode_noalloc_fwd",
             "attn_decode_workspace_bytes", "attn_status_str", "attn_last_hip_error"} <= set(names)
     for n in names:
         assert hasattr(lib, n), f"libattn.so does not export {n}"
@@ -91,6 +91,40 @@ def test_prefill_empty_is_noop(lib):
 ])
 def test_decode_rejects(lib, kw, code):
     assert decode(**kw) == code
+
+
+def decode_noalloc(q=P, k=P, v=P, o=P, B=1, Hq=2, Hkv=2, Sq=1, Skv=8, d=64, causal=0, scale=0.125,
+                   lens=NULL, dtype=attn.ATTN_BF16):
+    return attn.attn_decode_noalloc_fwd(q, k, v, o, B, Hq, Hkv, Sq, Skv, d, causal, scale, lens,
+                                        dtype, NULL)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=NULL), 1), (dict(o=NULL), 1), (dict(k=NULL), 1),
+    (dict(Sq=2), 2), (dict(Hq=6, Hkv=4), 2), (dict(B=-3), 2),
+    (dict(dtype=attn.ATTN_F32), 3), (dict(d=32), 3), (dict(d=256), 3), (dict(Hq=6, Hkv=2), 3),
+    (dict(q=MIS), 4), (dict(scale=math.nan), 7),
+    # partials beyond the static scratch: B*H_q chunked splits of (d + 1) floats
+    (dict(B=2048, Hq=32, Hkv=32, Skv=4096, d=128), 5),
+])
+def test_decode_noalloc_rejects(lib, kw, code):
+    """The allocation-free decode validates on the host, before it looks up
+    its scratch, and refuses sizes whose partials exceed the scratch."""
+    assert decode_noalloc(**kw) == code
+
+
+def test_decode_noalloc_scratch_limit(lib):
+    """The workloads' decodes fit the static scratch; the rejected shape above
+    does not."""
+    lim = attn.ATTN_DECODE_NOALLOC_SCRATCH_BYTES
+    assert re.search(r"ATTN_DECODE_NOALLOC_SCRATCH_BYTES\s+\(\(size_t\)32 << 20\)", open(HEADER).read())
+    assert attn.attn_decode_workspace_bytes(64, 32, 32, 4096, 128) <= lim
+    assert attn.attn_decode_workspace_bytes(128, 32, 8, 8192, 128) <= lim
+    assert attn.attn_decode_workspace_bytes(2048, 32, 32, 4096, 128) > lim
+
+
+def test_decode_noalloc_empty_is_noop(lib):
+    assert decode_noalloc(q=NULL, o=NULL, B=0) == 0
 
 
 def prefill_rope(q=P, k=P, v=P, o=P, B=1, Hq=2, Hkv=2, Sq=8, Skv=8, d=64, causal=1, scale=0.125,
