@@ -22,13 +22,15 @@
 //     O^T += V^T P^T over 32 keys (k-index 8g + j is key 4g + j for j < 4 and
 //     16 + 4g + j - 4 otherwise; V^T is read in that order with the LDS
 //     transpose read, so the sum is unchanged).
-//   - LDS rows (512 bytes) are XOR-swizzled at 16-byte granularity:
-//     slot s of row r is stored at s ^ sw(r), sw(r) = 2 (r & 7) | (r >> 3) & 1.
-//     The K-operand read (16 consecutive rows, one slot each) then covers all
-//     64 banks, and so does the transpose read of V (8 consecutive rows, one
-//     aligned slot pair each) by address; the hardware still spends one extra
-//     pass on each transpose read of this layout, whose two 16-lane groups
-//     read different rows of the same columns (measured with two swizzles).
+//   - LDS rows (512 bytes) are XOR-swizzled at 16-byte granularity: slot s of
+//     row r is stored at s ^ sw(r), sw(r) = 2 ((r & 7) ^ ((r >> 1) & 4)) |
+//     (r >> 3) & 1.  The K-operand read (16 consecutive rows, one slot each)
+//     covers 16 distinct slots.  In the transpose read of V the 16-lane group
+//     g addresses rows 4g .. 4g + 3 (and those + 16) of the same two slots;
+//     the term (r >> 1) & 4 gives rows 8 apart (groups g and g + 2) disjoint
+//     slot pairs, as it does rows 4 apart.  With sw(r) = 2 (r & 7) | (r >> 3) & 1
+//     alone every transpose read took one extra pass (SQ_LDS_BANK_CONFLICT
+//     68.2 M cycles per B4 H16 S4096 dispatch); with the term, 0.
 //   - LDS reads are issued ahead of the MFMAs that consume them (K one
 //     k-step, V^T four MFMAs), each MFMA with its reads one scheduling region.
 //   - Softmax in base 2 with the scale folded into the exponent's FMA, lazy
@@ -73,7 +75,7 @@ static_assert(kCopyRows % 16 == 0, "every copy round starts on the same swizzle 
 constexpr int KPF = 1;
 constexpr int VPF = 4;
 
-__device__ __forceinline__ int sw(int r) { return ((r & 7) << 1) | ((r >> 3) & 1); }
+__device__ __forceinline__ int sw(int r) { return (((r & 7) ^ ((r >> 1) & 4)) << 1) | ((r >> 3) & 1); }
 // byte offset of (row, 16-byte slot) inside a swizzled stage
 __device__ __forceinline__ uint32_t off(int row, int slot) {
   return (uint32_t)(row * kSlots + (slot ^ sw(row))) * 16u;
