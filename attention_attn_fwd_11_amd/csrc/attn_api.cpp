@@ -207,15 +207,14 @@ attn_status_t run_decode(const void* q, const void* k, const void* v, void* o, i
   p.n_split = (S_kv + p.chunk - 1) / p.chunk;
   p.n_wg = 0;
   if (decode_balanced(B, H_q, H_kv)) {
-    // Persistent grid: two workgroups per compute unit (the resident
-    // capacity: each stages a K and a V block per wave in LDS), never more
-    // than there are units.  The contiguous and the paged cache use the same
+    // Persistent grid: kDecodeWgPerCu workgroups per compute unit (the
+    // resident capacity), never more than there are units.  The contiguous and the paged cache use the same
     // grid, so both partition the keys alike and give the same bits.
     // Test-only override: ATTN_DECODE_WORKGROUPS.
     int dev = 0;
     const int cus = device_cus(&dev);
     if (cus <= 0) return hip_fail("hipDeviceGetAttribute(multiprocessor count)", hipGetLastError());
-    int64_t wg = 2 * (int64_t)cus;
+    int64_t wg = (int64_t)attn::kDecodeWgPerCu * cus;
     if (const char* env = std::getenv("ATTN_DECODE_WORKGROUPS")) {
       const long w = std::strtol(env, nullptr, 10);
       if (w >= 1 && w <= (1 << 20)) wg = w;

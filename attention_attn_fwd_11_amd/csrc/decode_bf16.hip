@@ -43,6 +43,106 @@ __device__ __forceinline__ void wait_vmem_below() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
+// Waits until this wave's LDS reads have returned their data.
+__device__ __forceinline__ void wait_lds() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
+// LDS byte address of a generic pointer into shared memory.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) void*)p));
+}
+
+// The score MFMA's K operand from LDS: 16-byte reads at a[ks] and a[ks] + HALF
+// (the same slots 16 rows further on) into x[0][ks] and x[1][ks], in one block
+// that waits for its own reads.  The compiler then sees no LDS read here and
+// inserts no wait for direct copies still in flight into other LDS buffers
+// (it cannot tell those buffers apart and would wait for every copy); the
+// caller waits for the copies into this buffer itself.
+template <int KS, int HALF>
+__device__ __forceinline__ void lds_read_k(u32x4 (&x)[2][KS], const uint32_t (&a)[KS]) {
+  static_assert(KS == 2 || KS == 4, "d = 64 or 128");
+  if constexpr (KS == 4) {
+    asm volatile(
+        "ds_read_b128 %0, %8\n\t"
+        "ds_read_b128 %1, %8 offset:%12\n\t"
+        "ds_read_b128 %2, %9\n\t"
+        "ds_read_b128 %3, %9 offset:%12\n\t"
+        "ds_read_b128 %4, %10\n\t"
+        "ds_read_b128 %5, %10 offset:%12\n\t"
+        "ds_read_b128 %6, %11\n\t"
+        "ds_read_b128 %7, %11 offset:%12\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(x[0][0]), "=&v"(x[1][0]), "=&v"(x[0][1]), "=&v"(x[1][1]), "=&v"(x[0][2]), "=&v"(x[1][2]),
+          "=&v"(x[0][3]), "=&v"(x[1][3])
+        : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "n"(HALF)
+        : "memory");
+  } else {
+    asm volatile(
+        "ds_read_b128 %0, %4\n\t"
+        "ds_read_b128 %1, %4 offset:%6\n\t"
+        "ds_read_b128 %2, %5\n\t"
+        "ds_read_b128 %3, %5 offset:%6\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(x[0][0]), "=&v"(x[1][0]), "=&v"(x[0][1]), "=&v"(x[1][1])
+        : "v"(a[0]), "v"(a[1]), "n"(HALF)
+        : "memory");
+  }
+}
+
+// The PV MFMA's V^T operand from LDS: for output tile t, transposed 4-row
+// reads at a[t] (rows 0..15 of the step) into lo[t] and at a[t] + HALF (rows
+// 16..31) into hi[t], in one block that waits for its own reads (for the same
+// reason as lds_read_k).
+template <int DT, int HALF>
+__device__ __forceinline__ void lds_read_vt(u32x2 (&lo)[DT], u32x2 (&hi)[DT], const uint32_t (&a)[DT]) {
+  static_assert(DT == 4 || DT == 8, "d = 64 or 128");
+  if constexpr (DT == 8) {
+    asm volatile(
+        "ds_read_b64_tr_b16 %0, %16\n\t"
+        "ds_read_b64_tr_b16 %1, %16 offset:%24\n\t"
+        "ds_read_b64_tr_b16 %2, %17\n\t"
+        "ds_read_b64_tr_b16 %3, %17 offset:%24\n\t"
+        "ds_read_b64_tr_b16 %4, %18\n\t"
+        "ds_read_b64_tr_b16 %5, %18 offset:%24\n\t"
+        "ds_read_b64_tr_b16 %6, %19\n\t"
+        "ds_read_b64_tr_b16 %7, %19 offset:%24\n\t"
+        "ds_read_b64_tr_b16 %8, %20\n\t"
+        "ds_read_b64_tr_b16 %9, %20 offset:%24\n\t"
+        "ds_read_b64_tr_b16 %10, %21\n\t"
+        "ds_read_b64_tr_b16 %11, %21 offset:%24\n\t"
+        "ds_read_b64_tr_b16 %12, %22\n\t"
+        "ds_read_b64_tr_b16 %13, %22 offset:%24\n\t"
+        "ds_read_b64_tr_b16 %14, %23\n\t"
+        "ds_read_b64_tr_b16 %15, %23 offset:%24\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(lo[0]), "=&v"(hi[0]), "=&v"(lo[1]), "=&v"(hi[1]), "=&v"(lo[2]), "=&v"(hi[2]),
+          "=&v"(lo[3]), "=&v"(hi[3]), "=&v"(lo[4]), "=&v"(hi[4]), "=&v"(lo[5]), "=&v"(hi[5]),
+          "=&v"(lo[6]), "=&v"(hi[6]), "=&v"(lo[7]), "=&v"(hi[7])
+        : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]), "v"(a[7]), "n"(HALF)
+        : "memory");
+  } else {
+    asm volatile(
+        "ds_read_b64_tr_b16 %0, %8\n\t"
+        "ds_read_b64_tr_b16 %1, %8 offset:%12\n\t"
+        "ds_read_b64_tr_b16 %2, %9\n\t"
+        "ds_read_b64_tr_b16 %3, %9 offset:%12\n\t"
+        "ds_read_b64_tr_b16 %4, %10\n\t"
+        "ds_read_b64_tr_b16 %5, %10 offset:%12\n\t"
+        "ds_read_b64_tr_b16 %6, %11\n\t"
+        "ds_read_b64_tr_b16 %7, %11 offset:%12\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(lo[0]), "=&v"(hi[0]), "=&v"(lo[1]), "=&v"(hi[1]), "=&v"(lo[2]), "=&v"(hi[2]),
+          "=&v"(lo[3]), "=&v"(hi[3])
+        : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "n"(HALF)
+        : "memory");
+  }
+}
+
+// Read-only int32 from device memory through the constant address space: a
+// wave-uniform address becomes a scalar load, which waits on no vector load.
+__device__ __forceinline__ int32_t ld_const(const int32_t* p) {
+  return *(const __attribute__((address_space(4))) int32_t*)p;
+}
+
 // First element of key row j of head (b, hk) in tensor t (K or V): the
 // contiguous cache [B, Hkv, Skv, d], or the page that holds row j.  Every
 // step of the split kernels covers at most 64 keys starting at a multiple of
@@ -56,7 +156,7 @@ __device__ __forceinline__ const uint16_t* kv_row(const void* t, const DecodePar
                                                   int j) {
   const uint16_t* base = static_cast<const uint16_t*>(t);
   if (!p.block_table) return base + (((int64_t)b * p.Hkv + hk) * p.Skv + j) * D;
-  int pg = p.block_table[(int64_t)b * p.max_blocks + j / p.page_size];
+  int pg = ld_const(p.block_table + (int64_t)b * p.max_blocks + j / p.page_size);
   pg = min(max(pg, 0), p.num_pages - 1);
   return base + (((int64_t)pg * p.Hkv + hk) * p.page_size + j % p.page_size) * D;
 }
@@ -488,7 +588,7 @@ __device__ __forceinline__ void unit_prefix(const DecodeParams& p, int* pre, int
 }
 
 template <int D, int G>
-__global__ __launch_bounds__(kThreads, 2) void decode_split_balanced(DecodeParams p) {
+__global__ __launch_bounds__(kThreads, kDecodeWgPerCu) void decode_split_balanced(DecodeParams p) {
   constexpr int KS = D / 32;          // k-steps of the score MFMA (32 features each)
   constexpr int DT = D / 16;          // 16-feature output tiles
   constexpr int SLOTS = D / 8;        // 16-byte slots per V row
@@ -500,22 +600,43 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_balanced(DecodeParam
   __shared__ __attribute__((aligned(16))) unsigned char kbuf[kWaves][VBYTES];
   __shared__ float mrg_m[kWaves][16];
   __shared__ float mrg_l[kWaves][16];
-  __shared__ int pre[kDecodeMaxBatch + 1];
   __shared__ int wave_tot[kWaves];
+  extern __shared__ int pre[];         // [B + 1], dynamic
   float (*mrg_o)[G][D] = reinterpret_cast<float (*)[G][D]>(&vbuf[0][0]);
 
   unit_prefix(p, pre, wave_tot);
-  const int U = pre[p.B];
+  // Work coordinates are kept wave-uniform (scalar registers), so length and
+  // page-table reads are scalar loads that never wait on the copies in flight.
+  const int U = __builtin_amdgcn_readfirstlane(pre[p.B]);
   const int R = (U + (int)gridDim.x - 1) / (int)gridDim.x;
   int u = (int)blockIdx.x * R;
   const int uend = min(u + R, U);
   if (u >= uend) return;                               // uniform across the workgroup
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int qcol = lane & 15;          // query column (valid if < G)
   const int grp = lane >> 4;           // 16-lane group
   unsigned char* vb = vbuf[wave];
   unsigned char* kb = kbuf[wave];
+  // LDS addresses of this lane's K-operand slots (row qcol, features
+  // 32*ks + 8*grp .. +7).
+  uint32_t k_addr[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks)
+    k_addr[ks] = lds_addr(kb + (qcol * SLOTS + ((4 * ks + grp) ^ (lds_swizzle(qcol) & (SLOTS - 1)))) * 16);
+  // LDS addresses of this lane's transposed V reads: output tile t, source
+  // lane (lane & 15) names row 4*grp + (lane&15)/4 and columns 16*t +
+  // 4*(lane%4) .. +3 (rows r and r + 16 share a swizzle).
+  uint32_t v_addr[DT];
+#pragma unroll
+  for (int t = 0; t < DT; ++t) {
+    const int src = lane & 15;
+    const int cidx = 16 * t + 4 * (src & 3);
+    const int cslot = cidx >> 3, cbyte = (cidx & 7) * 2;
+    const int r0 = 4 * grp + (src >> 2);
+    v_addr[t] = lds_addr(vb + (r0 * SLOTS + (cslot ^ (lds_swizzle(r0) & (SLOTS - 1)))) * 16 + cbyte);
+  }
   // V copy w puts this lane's 16 bytes at LDS row v_row0 + w*kRowsPerCopy,
   // physical slot v_phys; the swizzle of that row picks the logical slot.
   constexpr int kRowsPerCopy = 1024 / (2 * D);
@@ -530,28 +651,36 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_balanced(DecodeParam
   int lo = 0, hi = p.B - 1;
   while (lo < hi) {
     const int mid = (lo + hi + 1) >> 1;
-    if (pre[mid] <= u) lo = mid; else hi = mid - 1;
+    if (__builtin_amdgcn_readfirstlane(pre[mid]) <= u) lo = mid; else hi = mid - 1;
   }
   int b = lo;
-  int units_b = (pre[b + 1] - pre[b]) / p.Hkv;
-  int hk = (u - pre[b]) / units_b;
-  int k = (u - pre[b]) % units_b;
+  int pre_b = __builtin_amdgcn_readfirstlane(pre[b]);
+  int units_b = (__builtin_amdgcn_readfirstlane(pre[b + 1]) - pre_b) / p.Hkv;
+  int hk = (u - pre_b) / units_b;
+  int k = (u - pre_b) % units_b;
 
   while (u < uend) {
     int n = p.Skv;
-    if (p.kv_lens) n = min(max(p.kv_lens[b], 0), p.Skv);
+    if (p.kv_lens) n = min(max(ld_const(p.kv_lens + b), 0), p.Skv);
     const int seg_start = u;
-    const int seg_end = min(uend, pre[b] + (hk + 1) * units_b);
+    const int seg_end = min(uend, pre_b + (hk + 1) * units_b);
 
     // Q^T as B operand: lane (qcol, grp) holds Q[h0 + qcol][32*ks + 8*grp .. +7].
     bf16x8 qreg[KS];
     {
       const uint16_t* qp = static_cast<const uint16_t*>(p.q) + ((int64_t)b * p.Hq + (int64_t)hk * G) * D;
+      u32x4 w[KS];
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        u32x4 w = {0u, 0u, 0u, 0u};
-        if (qcol < G) w = ld16(qp + (int64_t)qcol * D + 32 * ks + 8 * grp);
-        qreg[ks] = as_bf16x8(w);
+        w[ks] = u32x4{0u, 0u, 0u, 0u};
+        if (qcol < G) w[ks] = ld16(qp + (int64_t)qcol * D + 32 * ks + 8 * grp);
+      }
+      // Use the values here, so the wait for the Q loads is placed now and
+      // not before every score MFMA of the step loop.
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        asm volatile("" ::"v"(w[ks]));
+        qreg[ks] = as_bf16x8(w[ks]);
       }
     }
     f32x4 oacc[DT];
@@ -559,51 +688,49 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_balanced(DecodeParam
     for (int t = 0; t < DT; ++t) oacc[t] = f32x4{};
     float m = kNegInf, lsum = 0.f;
 
-    for (; u < seg_end; ++u, ++k) {
-      const int base = k * kDecodeUnit + wave * 32;
-      if (base >= n) continue;                         // this wave's slice is past the length
-      // K then V straight into this wave's LDS regions by direct copies (copy
-      // w lands lane i at byte w*1024 + 16*i): each copy reads whole rows,
-      // 1 KiB contiguous, where loading K into the MFMA operand layout would
-      // touch 16 rows per instruction.  Rows past the length repeat row n-1.
-      const uint16_t* kp = kv_row<D>(p.k, p, b, hk, base);   // rows base .. base+31
-      const uint16_t* vp = kv_row<D>(p.v, p, b, hk, base);
+    // This wave's steps in the segment: units k0 .. k0 + nst - 1, those whose
+    // 32-key slice starts below the length.
+    const int k0 = k;
+    const int lim = n - wave * 32;
+    const int nst = lim > 0 ? max(0, min(seg_end - seg_start, (lim + kDecodeUnit - 1) / kDecodeUnit - k0)) : 0;
+    // K or V rows base .. base+31 straight into this wave's LDS region dst by
+    // direct copies (copy w lands lane i at byte w*1024 + 16*i): each copy
+    // reads whole rows, 1 KiB contiguous, where loading K into the MFMA
+    // operand layout would touch 16 rows per instruction.  Rows past the
+    // length repeat row n-1.
+    auto issue = [&](unsigned char* dst, const void* t, int base) __attribute__((always_inline)) {
+      const char* src = reinterpret_cast<const char*>(kv_row<D>(t, p, b, hk, base));
       if (base + 32 <= n) {
-        const char* kbs = reinterpret_cast<const char*>(kp);
-        const char* vbs = reinterpret_cast<const char*>(vp);
 #pragma unroll
         for (int w = 0; w < VP; ++w)
-          global_to_lds16_stream(kbs + (v_row0 + w * kRowsPerCopy) * 2 * D + v_slot(w) * 16, kb + w * 1024);
-#pragma unroll
-        for (int w = 0; w < VP; ++w)
-          global_to_lds16_stream(vbs + (v_row0 + w * kRowsPerCopy) * 2 * D + v_slot(w) * 16, vb + w * 1024);
+          global_to_lds16_stream(src + (v_row0 + w * kRowsPerCopy) * 2 * D + v_slot(w) * 16, dst + w * 1024);
       } else {
 #pragma unroll
         for (int w = 0; w < VP; ++w) {
           const int key = min(base + v_row0 + w * kRowsPerCopy, n - 1) - base;
-          global_to_lds16_stream(reinterpret_cast<const char*>(kp + key * D) + v_slot(w) * 16,
-                          kb + w * 1024);
-        }
-#pragma unroll
-        for (int w = 0; w < VP; ++w) {
-          const int key = min(base + v_row0 + w * kRowsPerCopy, n - 1) - base;
-          global_to_lds16_stream(reinterpret_cast<const char*>(vp + key * D) + v_slot(w) * 16,
-                          vb + w * 1024);
+          global_to_lds16_stream(src + key * 2 * D + v_slot(w) * 16, dst + w * 1024);
         }
       }
-      wait_vmem_below<VP>();   // the K copies have landed (the V copies may be in flight)
+    };
+    // Software pipeline: a buffer is refilled with the next step's rows as
+    // soon as this step has read it, so the next K copies fly during this
+    // step's softmax and PV, and the next V copies during the next scores.
+    // Outstanding copies are always K(i) then V(i), or V(i) then K(i+1).
+    if (nst > 0) {
+      issue(kb, p.k, k0 * kDecodeUnit + wave * 32);
+      issue(vb, p.v, k0 * kDecodeUnit + wave * 32);
+    }
+    for (int i = 0; i < nst; ++i) {
+      const int base = (k0 + i) * kDecodeUnit + wave * 32;
+      const bool more = i + 1 < nst;
+      wait_vmem_below<VP>();   // K(i) has landed (V(i) may be in flight)
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
       // K rows into the A-operand layout: lane (qcol, grp) takes row
       // 16*hlf + qcol, features 32*ks + 8*grp .. +7.
+      // (Rows r and r + 16 share a swizzle, so the second half is 16 rows on.)
       u32x4 kr[2][KS];
-#pragma unroll
-      for (int hlf = 0; hlf < 2; ++hlf) {
-        const int r = 16 * hlf + qcol;
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-          kr[hlf][ks] = *reinterpret_cast<const u32x4*>(
-              kb + (r * SLOTS + ((4 * ks + grp) ^ (lds_swizzle(r) & (SLOTS - 1)))) * 16);
-      }
+      lds_read_k<KS, 16 * SLOTS * 16>(kr, k_addr);
+      if (more) issue(kb, p.k, base + kDecodeUnit);   // the K reads have returned: refill
       f32x4 sacc[2];
 #pragma unroll
       for (int hlf = 0; hlf < 2; ++hlf) {
@@ -617,10 +744,10 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_balanced(DecodeParam
 #pragma unroll
       for (int hlf = 0; hlf < 2; ++hlf)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int key = base + 16 * hlf + 4 * grp + i;
-          const float s = key < n ? sacc[hlf][i] * p.scale_log2 : kNegInf;
-          sacc[hlf][i] = s;
+        for (int e = 0; e < 4; ++e) {
+          const int key = base + 16 * hlf + 4 * grp + e;
+          const float s = key < n ? sacc[hlf][e] * p.scale_log2 : kNegInf;
+          sacc[hlf][e] = s;
           tmax = fmaxf(tmax, s);
         }
       tmax = fmaxf(tmax, shfl_xor(tmax, 16));
@@ -641,23 +768,22 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_balanced(DecodeParam
 #pragma unroll
       for (int t = 0; t < DT; ++t) oacc[t] *= alpha;
 
-      wait_vmem();       // this wave's V copies have landed in its LDS region
+      if (more) wait_vmem_below<VP>();   // V(i) has landed (K(i+1) may be in flight)
+      else wait_vmem();
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-      const int src = lane & 15;
+      u32x2 vlo[DT], vhi[DT];
+      lds_read_vt<DT, 16 * SLOTS * 16>(vlo, vhi, v_addr);
 #pragma unroll
-      for (int t = 0; t < DT; ++t) {
-        const int cidx = 16 * t + 4 * (src & 3);
-        const int cslot = cidx >> 3, cbyte = (cidx & 7) * 2;
-        const int r0 = 4 * grp + (src >> 2);
-        const int r1 = r0 + 16;
-        const u32x2 lo2 = lds_read_tr16x4(vb + (r0 * SLOTS + (cslot ^ (lds_swizzle(r0) & (SLOTS - 1)))) * 16 + cbyte);
-        const u32x2 hi2 = lds_read_tr16x4(vb + (r1 * SLOTS + (cslot ^ (lds_swizzle(r1) & (SLOTS - 1)))) * 16 + cbyte);
-        oacc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(u32x4{lo2[0], lo2[1], hi2[0], hi2[1]}), pb, oacc[t], 0, 0, 0);
+      for (int t = 0; t < DT; ++t)
+        oacc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(u32x4{vlo[t][0], vlo[t][1], vhi[t][0], vhi[t][1]}),
+                                                          pb, oacc[t], 0, 0, 0);
+      if (more) {
+        wait_lds();            // the V reads are in registers: refill the buffer
+        issue(vb, p.v, base + kDecodeUnit);
       }
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     }
+    k = k0 + (seg_end - seg_start);
+    u = seg_end;
 
     // Flush the segment: merge the waves, write one partial per query head.
     lsum += shfl_xor(lsum, 16);
@@ -696,8 +822,11 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_balanced(DecodeParam
     k = 0;
     if (++hk == p.Hkv) {
       hk = 0;
-      do { ++b; } while (b < p.B && pre[b + 1] == pre[b]);
-      if (b < p.B) units_b = (pre[b + 1] - pre[b]) / p.Hkv;
+      do { ++b; } while (b < p.B && __builtin_amdgcn_readfirstlane(pre[b + 1]) == __builtin_amdgcn_readfirstlane(pre[b]));
+      if (b < p.B) {
+        pre_b = __builtin_amdgcn_readfirstlane(pre[b]);
+        units_b = (__builtin_amdgcn_readfirstlane(pre[b + 1]) - pre_b) / p.Hkv;
+      }
     }
   }
 }
@@ -788,7 +917,8 @@ __global__ __launch_bounds__(64) void decode_combine(DecodeParams p) {
 
 template <int D, int G>
 hipError_t launch_balanced(const DecodeParams& p, hipStream_t stream) {
-  hipLaunchKernelGGL((decode_split_balanced<D, G>), dim3(p.n_wg), dim3(kThreads), 0, stream, p);
+  hipLaunchKernelGGL((decode_split_balanced<D, G>), dim3(p.n_wg), dim3(kThreads), (p.B + 1) * sizeof(int),
+                     stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((decode_combine_balanced<D, G>), dim3(p.Hq, p.B), dim3(64), 0, stream, p);
@@ -830,3 +960,4 @@ hipError_t launch_decode_bf16(const DecodeParams& p, hipStream_t stream) {
 }
 
 }  // namespace attn
+

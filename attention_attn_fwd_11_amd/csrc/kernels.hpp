@@ -65,6 +65,10 @@ struct DecodeParams {
 // Largest batch the balanced (G >= 2) decode pass handles: its workgroups
 // keep a prefix sum of per-batch work in LDS.
 constexpr int kDecodeMaxBatch = 2048;
+// Resident workgroups per compute unit the balanced decode pass is built for
+// (its register bound) and launched with (its persistent grid): each stages
+// a K and a V block per wave in LDS, 64 KiB per workgroup.
+constexpr int kDecodeWgPerCu = 2;
 // Keys per work unit of the balanced decode pass (4 waves x 32 keys).
 constexpr int kDecodeUnit = 128;
 // Most workgroups of the balanced decode pass; its partials need at most
