@@ -82,7 +82,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=5.0,
                     help="target CPU time of the oracle sample of each large prefill")
     ap.add_argument("--only", default=None,
-                    help="time one named workload only and print its line (for profiling)")
+                    help="time one named workload only and print its line (for profiling); "
+                         "decode_graph_small runs the eager-versus-graph decode comparison")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="with --only: afterwards run a plain device copy of this many MiB "
                          "(3 times), the reference for calibrating HBM byte counters")
@@ -347,10 +348,14 @@ def paged_decode(torch, attn, wl, x, w, steps, warmup, page_size=128):
             "pages": sum((int(n) + page_size - 1) // page_size for n in lens.cpu().tolist())}
 
 
-def decode_graph(torch, attn, wl, dev, steps=200):
+def decode_graph(torch, attn, wl, dev, steps=192):
     """Launch overhead of a small decode step (B1 H32 L4096 d128, 64 MiB of
-    cache): host wall time per step over `steps` back-to-back eager calls
-    against `steps` replays of the same call captured in a HIP graph."""
+    cache): host wall time per step over `steps` back-to-back eager calls,
+    against replays of the same call captured in a HIP graph, one step per
+    graph and 16 steps per graph; and the host time to issue one eager call
+    and one replay (without waiting for the GPU).  A replay costs more host
+    time than this step's kernels take, so one-step replays leave the GPU idle
+    between steps; capturing several steps per graph amortises that cost."""
     B, H, L, d = 1, 32, 4096, 128
     x = wl.random_problem(B, H, H, 1, L, d, dtype="bf16", device=dev, seed=7)
     lens = torch.full((B,), L, dtype=torch.int32, device=dev)
@@ -364,25 +369,42 @@ def decode_graph(torch, attn, wl, dev, steps=200):
             f()
     torch.cuda.current_stream().wait_stream(side)
     torch.cuda.synchronize()
-    g = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g):
-        f()
+    graphs = {}
+    for k in (1, 16):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(k):
+                f()
+        graphs[k] = g
     torch.cuda.synchronize()
 
-    def wall(fn):
-        for _ in range(20):
+    def wall(fn, calls, per_call):
+        for _ in range(10):
             fn()
         torch.cuda.synchronize()
         t0 = time.perf_counter()
-        for _ in range(steps):
+        for _ in range(calls):
             fn()
         torch.cuda.synchronize()
-        return (time.perf_counter() - t0) / steps * 1e6
+        return (time.perf_counter() - t0) / (calls * per_call) * 1e6
 
-    eager_us = wall(f)
-    graph_us = wall(g.replay)
+    def issue(fn, calls=32):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(calls):
+            fn()
+        t = (time.perf_counter() - t0) / calls * 1e6
+        torch.cuda.synchronize()
+        return t
+
+    eager_us = wall(f, steps, 1)
+    graph_us = wall(graphs[1].replay, steps, 1)
+    graph16_us = wall(graphs[16].replay, steps // 16, 16)
     return {"shape": f"decode bf16 B{B} Hq{H} Hkv{H} Sq1 Skv{L} d{d}", "steps": steps,
             "eager_us_per_step": round(eager_us, 2), "graph_us_per_step": round(graph_us, 2),
+            "graph16_us_per_step": round(graph16_us, 2),
+            "host_us_per_eager_call": round(issue(f), 2),
+            "host_us_per_replay": round(issue(graphs[1].replay), 2),
             "kv_bytes": 2 * B * H * L * d * 2}
 
 
@@ -445,6 +467,9 @@ def main():
         sys.exit(1)
     dev = "cuda:0"
     torch.cuda.set_device(0)
+    if args.only == "decode_graph_small":
+        print(json.dumps(decode_graph(torch, attn, wl, dev)), flush=True)
+        return
     if args.only:
         return only(args, torch, attn, wl, dev)
 
