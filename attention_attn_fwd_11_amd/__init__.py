@@ -9,6 +9,7 @@ output, pass torch's current HIP stream and keep a decode workspace per
 no fallback path: the library is loaded on first use, and every entry point
 raises ImportError if libattn.so has not been built.
 """
+import contextlib
 import ctypes
 import math
 import os
@@ -22,7 +23,7 @@ __all__ = [
     "attn_prefill_varlen_fwd", "attn_prefill_rope_fwd",
     "attn_prefill_rope_workspace_bytes", "attn_decode_workspace_bytes",
     "attn_status_str", "attn_last_hip_error", "prefill", "prefill_varlen", "decode",
-    "decode_paged", "library_path",
+    "decode_paged", "library_path", "lds_poison_library_path", "use_library",
 ]
 
 ATTN_F32 = 0
@@ -32,6 +33,9 @@ STATUS = {0: "ATTN_OK", 1: "ATTN_ERR_NULL", 2: "ATTN_ERR_SHAPE", 3: "ATTN_ERR_UN
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 library_path = os.path.join(_HERE, "libattn.so")
+# The same library with each direct global -> LDS copy preceded by a NaN fill
+# of its destination (a debug build for the tests; see use_library).
+lds_poison_library_path = os.path.join(_HERE, "libattn_lds_poison.so")
 
 _lib = None
 _lock = threading.Lock()
@@ -48,37 +52,58 @@ def _load():
             raise ImportError(
                 f"{library_path} is missing: build it with "
                 "`python -m attention_attn_fwd_11_amd.build` (hipcc, gfx950)")
-        # torch is imported first so the library binds to the HIP runtime torch loaded.
-        lib = ctypes.CDLL(library_path)
-        vp, i32, f32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
-        lib.attn_prefill_fwd.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, f32,
-                                         vp, ctypes.c_int, vp]
-        lib.attn_prefill_fwd.restype = ctypes.c_int
-        lib.attn_decode_fwd.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, f32,
-                                        vp, ctypes.c_int, vp, sz, vp]
-        lib.attn_decode_fwd.restype = ctypes.c_int
-        lib.attn_prefill_varlen_fwd.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32,
-                                                i32, i32, i32, f32, ctypes.c_int, vp]
-        lib.attn_prefill_varlen_fwd.restype = ctypes.c_int
-        lib.attn_prefill_rope_fwd.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, f32,
-                                              vp, vp, i32, vp, ctypes.c_size_t, ctypes.c_int, vp]
-        lib.attn_prefill_rope_workspace_bytes.argtypes = [i32, i32, i32, i32]
-        lib.attn_prefill_rope_workspace_bytes.restype = ctypes.c_size_t
-        lib.attn_prefill_rope_fwd.restype = ctypes.c_int
-        lib.attn_decode_noalloc_fwd.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32,
-                                                f32, vp, ctypes.c_int, vp]
-        lib.attn_decode_noalloc_fwd.restype = ctypes.c_int
-        lib.attn_decode_paged_fwd.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, f32, vp, i32, i32,
-                                              i32, vp, ctypes.c_int, vp, sz, vp]
-        lib.attn_decode_paged_fwd.restype = ctypes.c_int
-        lib.attn_decode_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
-        lib.attn_decode_workspace_bytes.restype = sz
-        lib.attn_status_str.argtypes = [ctypes.c_int]
-        lib.attn_status_str.restype = ctypes.c_char_p
-        lib.attn_last_hip_error.argtypes = []
-        lib.attn_last_hip_error.restype = ctypes.c_char_p
-        _lib = lib
+        _lib = _open(library_path)
     return _lib
+
+
+def _open(path):
+    """Load one build of the library and declare its entry points."""
+    # torch is imported first so the library binds to the HIP runtime torch loaded.
+    lib = ctypes.CDLL(path)
+    vp, i32, f32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
+    lib.attn_prefill_fwd.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, f32,
+                                     vp, ctypes.c_int, vp]
+    lib.attn_prefill_fwd.restype = ctypes.c_int
+    lib.attn_decode_fwd.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, f32,
+                                    vp, ctypes.c_int, vp, sz, vp]
+    lib.attn_decode_fwd.restype = ctypes.c_int
+    lib.attn_prefill_varlen_fwd.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32,
+                                            i32, i32, i32, f32, ctypes.c_int, vp]
+    lib.attn_prefill_varlen_fwd.restype = ctypes.c_int
+    lib.attn_prefill_rope_fwd.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, f32,
+                                          vp, vp, i32, vp, ctypes.c_size_t, ctypes.c_int, vp]
+    lib.attn_prefill_rope_workspace_bytes.argtypes = [i32, i32, i32, i32]
+    lib.attn_prefill_rope_workspace_bytes.restype = ctypes.c_size_t
+    lib.attn_prefill_rope_fwd.restype = ctypes.c_int
+    lib.attn_decode_noalloc_fwd.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32,
+                                            f32, vp, ctypes.c_int, vp]
+    lib.attn_decode_noalloc_fwd.restype = ctypes.c_int
+    lib.attn_decode_paged_fwd.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, f32, vp, i32, i32,
+                                          i32, vp, ctypes.c_int, vp, sz, vp]
+    lib.attn_decode_paged_fwd.restype = ctypes.c_int
+    lib.attn_decode_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
+    lib.attn_decode_workspace_bytes.restype = sz
+    lib.attn_status_str.argtypes = [ctypes.c_int]
+    lib.attn_status_str.restype = ctypes.c_char_p
+    lib.attn_last_hip_error.argtypes = []
+    lib.attn_last_hip_error.restype = ctypes.c_char_p
+    return lib
+
+
+@contextlib.contextmanager
+def use_library(path):
+    """Run the wrappers on another build of the library inside the block (the
+    LDS-poison debug build, libattn_lds_poison.so, in the tests); the default
+    build is back in use afterwards.  Not for concurrent use."""
+    global _lib
+    other = _open(path)
+    with _lock:
+        prev, _lib = _lib, other
+    try:
+        yield other
+    finally:
+        with _lock:
+            _lib = prev
 
 
 # ---------------------------------------------------------------------------

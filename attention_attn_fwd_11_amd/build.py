@@ -1,5 +1,8 @@
-"""Build libattn.so (the gfx950 kernels and the C ABI) and libattn_probe.so
-(a streaming-read probe the benchmark uses for context), with hipcc.
+"""Build libattn.so (the gfx950 kernels and the C ABI), libattn_probe.so
+(a streaming-read probe the benchmark uses for context) and
+libattn_lds_poison.so (the same library with every direct global -> LDS copy
+preceded by a NaN fill of its destination, a debug build the tests use to
+catch missing waits and barriers), with hipcc.
 
     python -m attention_attn_fwd_11_amd.build
 
@@ -17,11 +20,15 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libattn.so")
 PROBE_LIB = os.path.join(PKG, "libattn_probe.so")
+POISON_LIB = os.path.join(PKG, "libattn_lds_poison.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 SOURCES = ["attn_api.cpp", "prefill_f32.hip", "prefill_bf16.hip", "prefill_d256.hip", "decode_bf16.hip",
            "util.hip", "rope_bf16.hip"]
 PROBE_SOURCES = ["read_probe.hip"]
+# Sources that stage tiles in LDS by direct copies: rebuilt with
+# ATTN_LDS_POISON for the poison library (the rest is shared).
+POISON_SOURCES = ["prefill_bf16.hip", "prefill_d256.hip", "decode_bf16.hip"]
 
 # Device code for gfx950 only.  Packed-fp32 instruction selection is switched
 # off on purpose: ordinary fp32 code is compiled to scalar-lane VALU ops.
@@ -45,8 +52,8 @@ SOURCE_FLAGS = {
 }
 
 
-def _compile(src, extra):
-    out = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
+def _compile(src, extra, suffix=""):
+    out = os.path.join(BUILD, os.path.splitext(src)[0] + suffix + ".o")
     lang = ["-x", "hip"] if src.endswith(".cpp") else []
     cmd = [HIPCC, *FLAGS, *SOURCE_FLAGS.get(src, []), *extra, *lang, "-c", os.path.join(CSRC, src),
            "-o", out]
@@ -69,17 +76,20 @@ def _link(objs, lib):
 
 
 def build(extra=(), verbose=False):
-    """Compile every source, link libattn.so and libattn_probe.so; returns the
-    path of libattn.so."""
+    """Compile every source, link libattn.so, libattn_probe.so and
+    libattn_lds_poison.so; returns the path of libattn.so."""
     os.makedirs(BUILD, exist_ok=True)
-    srcs = SOURCES + PROBE_SOURCES
-    with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
-        results = dict(zip(srcs, ex.map(lambda s: _compile(s, list(extra)), srcs)))
-    for obj, warn in results.values():
+    jobs = [(src, list(extra), "") for src in SOURCES + PROBE_SOURCES]
+    jobs += [(src, [*extra, "-DATTN_LDS_POISON"], "_lds_poison") for src in POISON_SOURCES]
+    with cf.ThreadPoolExecutor(max_workers=8) as ex:
+        outs = list(ex.map(lambda j: _compile(*j), jobs))
+    results = {(src, suffix): out for (src, _, suffix), out in zip(jobs, outs)}
+    for obj, warn in outs:
         if warn and verbose:
             print(warn, file=sys.stderr)
-    _link([results[s][0] for s in SOURCES], LIB)
-    _link([results[s][0] for s in PROBE_SOURCES], PROBE_LIB)
+    _link([results[(s, "")][0] for s in SOURCES], LIB)
+    _link([results[(s, "")][0] for s in PROBE_SOURCES], PROBE_LIB)
+    _link([results[(s, "_lds_poison" if s in POISON_SOURCES else "")][0] for s in SOURCES], POISON_LIB)
     return LIB
 
 

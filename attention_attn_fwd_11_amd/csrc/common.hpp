@@ -78,10 +78,28 @@ __device__ __forceinline__ int lds_swizzle(int row) {
   return ((row & 3) << 1) | ((row >> 2) & 1) | (row & 8);
 }
 
+// LDS-poison debug build (compiled with ATTN_LDS_POISON into
+// libattn_lds_poison.so): before a direct copy lands lane i's 16 bytes at
+// lds_base + 16*i, the lane writes bf16 NaNs there and waits for the write,
+// so any read of a staging buffer that is not ordered after the copy's
+// completion (a missing wait or barrier) returns NaN and fails parity instead
+// of silently reading the previous tile.  A no-op in the normal build.
+__device__ __forceinline__ void lds_poison_lane(void* lds_base) {
+#ifdef ATTN_LDS_POISON
+  const int lane = __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+  *reinterpret_cast<u32x4*>(static_cast<unsigned char*>(lds_base) + 16 * lane) =
+      u32x4{0x7fc17fc1u, 0x7fc17fc1u, 0x7fc17fc1u, 0x7fc17fc1u};
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#else
+  (void)lds_base;
+#endif
+}
+
 // Direct global -> LDS copy of 16 bytes per lane (global_load_lds_dwordx4):
 // lane i's 16 bytes land at lds_base + 16*i; lds_base must be wave-uniform.
 typedef __attribute__((address_space(3))) void lds_void;
 __device__ __forceinline__ void global_to_lds16(const void* g, void* lds_base) {
+  lds_poison_lane(lds_base);
   __builtin_amdgcn_global_load_lds(g, (lds_void*)lds_base, 16, 0, 0);
 }
 
@@ -92,6 +110,7 @@ __device__ __forceinline__ u32x4 ld16_stream(const void* p) {
   return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
 }
 __device__ __forceinline__ void global_to_lds16_stream(const void* g, void* lds_base) {
+  lds_poison_lane(lds_base);
   __builtin_amdgcn_global_load_lds(g, (lds_void*)lds_base, 16, 0, 2);   // cache policy 2: nt
 }
 
@@ -107,6 +126,7 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t raw_buffer(const void* base, i
 // lds_base + 16*i; lds_base must be wave-uniform (it goes to M0).
 __device__ __forceinline__ void buffer_to_lds16(__amdgpu_buffer_rsrc_t rsrc, void* lds_base, int32_t voff,
                                                 int32_t soff) {
+  lds_poison_lane(lds_base);
   __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)lds_base, 16, voff, soff, 0, 0);
 }
 
