@@ -334,7 +334,7 @@ def _decode_buffers(q, o, ws, need, others):
             raise ValueError(f"{name} must be on q's device ({q.device}), got {t.device}")
     if o is None:
         o = torch.empty_like(q)
-    _check_tensor("out", o, torch.bfloat16)
+    _check_tensor("out", o, q.dtype)
     if o.shape != q.shape or o.device != q.device:
         raise ValueError("out must have q's shape and device")
     if ws is None:
@@ -350,14 +350,17 @@ def _decode_buffers(q, o, ws, need, others):
 
 def decode(q, k_cache, v_cache, kv_lens=None, scale=None, out=None, workspace=None):
     """Single-query decode.  q [B,H_q,1,d]; k_cache, v_cache [B,H_kv,S_cap,d]
-    (bf16); kv_lens int32 [B] on the device (None: every row is valid).
+    (bf16, or all float32); kv_lens int32 [B] on the device (None: every row
+    is valid).
 
-    Returns o [B,H_q,1,d] bf16.  Runs the split and combine kernels on torch's
-    current stream; the workspace (if not given) is cached per (device,
-    stream), and must be given under graph capture.
+    Returns o [B,H_q,1,d] with q's dtype.  Runs the split and combine kernels
+    on torch's current stream; the workspace (if not given) is cached per
+    (device, stream), and must be given under graph capture.
     """
+    if q.dtype not in _DTYPES:
+        raise TypeError(f"unsupported dtype {q.dtype}")
     for name, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache)):
-        _check_tensor(name, t, torch.bfloat16)
+        _check_tensor(name, t, q.dtype)
         if t.dim() != 4:
             raise ValueError(f"{name} must be [B, H, S, d]")
     B, H_q, S_q, d = q.shape
@@ -372,7 +375,7 @@ def decode(q, k_cache, v_cache, kv_lens=None, scale=None, out=None, workspace=No
                             (("k_cache", k_cache), ("v_cache", v_cache)))
     stream = torch.cuda.current_stream(q.device).cuda_stream
     st = attn_decode_fwd(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(o), B, H_q, H_kv, S_q, S_kv,
-                         d, 0, float(scale), _ptr(lens), ATTN_BF16, _ptr(ws),
+                         d, 0, float(scale), _ptr(lens), _DTYPES[q.dtype], _ptr(ws),
                          ws.numel() * ws.element_size(), ctypes.c_void_p(stream))
     if st != 0:
         raise AttnError(st, "attn_decode_fwd")
@@ -381,16 +384,19 @@ def decode(q, k_cache, v_cache, kv_lens=None, scale=None, out=None, workspace=No
 
 def decode_paged(q, k_pages, v_pages, block_table, kv_lens=None, scale=None, out=None,
                  workspace=None):
-    """Single-query decode over a paged cache.  q [B,H_q,1,d] bf16; k_pages,
-    v_pages [num_pages,H_kv,page_size,d] bf16; block_table int32 [B,max_blocks]
-    (page of each sequence's page_size-key block); kv_lens int32 [B] or None.
+    """Single-query decode over a paged cache.  q [B,H_q,1,d]; k_pages,
+    v_pages [num_pages,H_kv,page_size,d] (bf16, or all float32); block_table
+    int32 [B,max_blocks] (page of each sequence's page_size-key block);
+    kv_lens int32 [B] or None.
 
-    Returns o [B,H_q,1,d] bf16, on torch's current stream; the workspace (if
-    not given) is cached per (device, stream), and must be given under graph
-    capture.
+    Returns o [B,H_q,1,d] with q's dtype, on torch's current stream; the
+    workspace (if not given) is cached per (device, stream), and must be given
+    under graph capture.
     """
+    if q.dtype not in _DTYPES:
+        raise TypeError(f"unsupported dtype {q.dtype}")
     for name, t in (("q", q), ("k_pages", k_pages), ("v_pages", v_pages)):
-        _check_tensor(name, t, torch.bfloat16)
+        _check_tensor(name, t, q.dtype)
         if t.dim() != 4:
             raise ValueError(f"{name} must be 4-dimensional")
     _check_tensor("block_table", block_table, torch.int32)
@@ -410,7 +416,7 @@ def decode_paged(q, k_pages, v_pages, block_table, kv_lens=None, scale=None, out
     stream = torch.cuda.current_stream(q.device).cuda_stream
     st = attn_decode_paged_fwd(_ptr(q), _ptr(k_pages), _ptr(v_pages), _ptr(o), B, H_q, H_kv, d,
                                float(scale), _ptr(block_table), max_blocks, page_size, num_pages,
-                               _ptr(lens), ATTN_BF16, _ptr(ws), ws.numel() * ws.element_size(),
+                               _ptr(lens), _DTYPES[q.dtype], _ptr(ws), ws.numel() * ws.element_size(),
                                ctypes.c_void_p(stream))
     if st != 0:
         raise AttnError(st, "attn_decode_paged_fwd")

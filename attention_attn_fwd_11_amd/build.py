@@ -24,7 +24,7 @@ POISON_LIB = os.path.join(PKG, "libattn_lds_poison.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 SOURCES = ["attn_api.cpp", "prefill_f32.hip", "prefill_bf16.hip", "prefill_d256.hip", "decode_bf16.hip",
-           "util.hip", "rope_bf16.hip"]
+           "decode_f32.hip", "util.hip", "rope_bf16.hip"]
 PROBE_SOURCES = ["read_probe.hip"]
 # Sources that stage tiles in LDS by direct copies: rebuilt with
 # ATTN_LDS_POISON for the poison library (the rest is shared).

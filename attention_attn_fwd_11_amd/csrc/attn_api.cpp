@@ -133,12 +133,13 @@ size_t workspace_bytes(int32_t B, int32_t H_q, int32_t H_kv, int32_t S_kv, int32
   return round_up(rows * d * sizeof(float), 256) + round_up(rows * sizeof(float), 256);
 }
 
-// What the decode kernels implement: bf16, d 64 or 128, query groups of
-// 1, 2, 4, 8 or 16 heads.
+// What the decode kernels implement: d 64 or 128; bf16 with query groups of
+// 1, 2, 4, 8 or 16 heads, fp32 with any group size.
 bool decode_supported(int32_t H_q, int32_t H_kv, int32_t d, attn_dtype_t dtype) {
   const int G = H_q / H_kv;
-  return dtype == ATTN_BF16 && (d == 64 || d == 128) &&
-         (G == 1 || G == 2 || G == 4 || G == 8 || G == 16);
+  if (d != 64 && d != 128) return false;
+  if (dtype == ATTN_F32) return true;
+  return dtype == ATTN_BF16 && (G == 1 || G == 2 || G == 4 || G == 8 || G == 16);
 }
 
 // Scratch of the allocation-free decode entry point (attn_decode_noalloc_fwd):
@@ -191,12 +192,39 @@ attn_status_t run_decode(const void* q, const void* k, const void* v, void* o, i
   if (B == 0) return ATTN_OK;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (S_kv == 0) {
-    hipError_t e = attn::launch_zero_fill(o, (size_t)B * H_q * d * 2, s);
+    const size_t elt = dtype == ATTN_F32 ? 4 : 2;
+    hipError_t e = attn::launch_zero_fill(o, (size_t)B * H_q * d * elt, s);
     return e == hipSuccess ? ATTN_OK : hip_fail("zero-fill launch", e);
   }
   const size_t need = workspace_bytes(B, H_q, H_kv, S_kv, d);
   if (!workspace || ws_bytes < need) return ATTN_ERR_WORKSPACE;
   if (!aligned16(workspace)) return ATTN_ERR_ALIGN;
+  if (dtype == ATTN_F32) {
+    // fp32: every query head streams its own chunks (the one-head-per-KV-head
+    // split policy applied to the query heads), with no more splits than the
+    // workspace that attn_decode_workspace_bytes sized holds (at least one
+    // per query head for every group size).  Chunks are multiples of 256 keys.
+    attn::DecodeParams p{};
+    p.q = q; p.k = k; p.v = v; p.o = o; p.kv_lens = kv_lens;
+    p.B = B; p.Hq = H_q; p.Hkv = H_kv; p.Skv = S_kv; p.d = d;
+    p.block_table = block_table; p.max_blocks = max_blocks; p.page_size = page_size;
+    p.num_pages = num_pages;
+    const size_t rows = partial_rows(B, H_q, H_kv, S_kv);
+    int64_t splits = (S_kv + decode_chunk(B, H_q, H_q, S_kv) - 1) / decode_chunk(B, H_q, H_q, S_kv);
+    const int64_t fit = (int64_t)(rows / ((size_t)B * H_q));
+    if (splits > fit) splits = fit;
+    if (splits < 1) splits = 1;
+    int64_t chunk = (S_kv + splits - 1) / splits;
+    chunk = (chunk + 255) / 256 * 256;
+    p.chunk = (int)chunk;
+    p.n_split = (int)((S_kv + chunk - 1) / chunk);
+    p.part_o = static_cast<float*>(workspace);
+    p.part_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                          round_up(rows * d * sizeof(float), 256));
+    p.scale_log2 = (float)((double)scale * 1.4426950408889634);
+    hipError_t e = attn::launch_decode_f32(p, s);
+    return e == hipSuccess ? ATTN_OK : hip_fail("decode launch", e);
+  }
 
   attn::DecodeParams p{};
   p.q = q; p.k = k; p.v = v; p.o = o; p.kv_lens = kv_lens;

@@ -80,6 +80,8 @@ hipError_t launch_prefill_bf16(const PrefillParams& p, hipStream_t stream);
 // d = 256 without the rotary embedding (16-row waves; called by launch_prefill_bf16)
 hipError_t launch_prefill_d256(const PrefillParams& p, hipStream_t stream);
 hipError_t launch_decode_bf16(const DecodeParams& p, hipStream_t stream);
+// fp32 inputs and output (chunked split + combine, one workgroup per query head)
+hipError_t launch_decode_f32(const DecodeParams& p, hipStream_t stream);
 hipError_t launch_zero_fill(void* dst, size_t bytes, hipStream_t stream);
 // Rotary embedding of key rows into dst (same [B, H, S, d] bf16 layout as
 // src): row j of every head at position j; rows j >= kv_lens[b] (when given)

@@ -168,7 +168,11 @@ attn_status_t attn_prefill_varlen_fwd(const void* q, const void* k, const void* 
  *   first clamp(kv_lens[b], 0, S_kv) rows.
  *   S_q must be 1 (else ATTN_ERR_SHAPE).  causal is accepted and has no
  *   effect with one query row (the bottom-right mask then allows every key).
- *   dtype: ATTN_BF16 only (else ATTN_ERR_UNSUPPORTED).  d: 64 or 128.
+ *   d: 64 or 128.  dtype: ATTN_BF16 with H_q/H_kv in {1, 2, 4, 8, 16}, or
+ *   ATTN_F32 with any H_q/H_kv (else ATTN_ERR_UNSUPPORTED); q, the caches and
+ *   o all have that dtype.  bf16 computes scores and P V with fp32
+ *   accumulation (P rounded to bf16 before P V on the matrix cores when
+ *   H_q > H_kv); fp32 computes in fp32 throughout.
  *   workspace: device memory of at least
  *   attn_decode_workspace_bytes(B, H_q, H_kv, S_kv, d) bytes, 16-byte
  *   aligned, for the per-split partial results (fp32).  Its contents need no
@@ -177,7 +181,9 @@ attn_status_t attn_prefill_varlen_fwd(const void* q, const void* k, const void* 
  *
  * Two kernels on `stream`: a split pass in which each workgroup streams one
  * chunk of the cache once and writes a normalised partial output with its
- * log-sum-exp, then a combine pass that merges the partials of each head.
+ * log-sum-exp, then a combine pass that merges the partials of each head
+ * (the one-head-per-KV-head and fp32 passes skip it when every head has a
+ * single split).
  * This is the Flash-Decoding split of "GPU learning day 24: Operator Fusion",
  * FAQ Q4, merged with the rescaling identity of that page's section 3.4 loop.
  */
@@ -224,9 +230,9 @@ attn_status_t attn_decode_noalloc_fwd(const void* q, const void* k_cache, const 
 /*
  * Single-query decode over a paged KV cache.
  *
- *   q [B,H_q,1,d], o [B,H_q,1,d]   (device, bf16)
+ *   q [B,H_q,1,d], o [B,H_q,1,d]   (device, dtype)
  *   k_pages, v_pages: page pools [num_pages, H_kv, page_size, d] (device,
- *   bf16); page p holds page_size consecutive key rows of every KV head.
+ *   dtype); page p holds page_size consecutive key rows of every KV head.
  *   block_table: device int32 [B, max_blocks]; key row j of sequence b is row
  *   j % page_size of page block_table[b * max_blocks + j / page_size].
  *   kv_lens: device int32[B] or NULL (NULL: every sequence has
@@ -237,8 +243,8 @@ attn_status_t attn_decode_noalloc_fwd(const void* q, const void* k_cache, const 
  *   memory outside the pools is read).
  *   page_size: a positive multiple of 128; max_blocks >= 1; num_pages >= 1
  *   (else ATTN_ERR_SHAPE).  max_blocks * page_size plays the role of S_kv in
- *   every other rule of attn_decode_fwd: the size limits, G = H_q/H_kv in
- *   {1, 2, 4, 8, 16}, dtype ATTN_BF16, d 64 or 128, and the workspace, which
+ *   every other rule of attn_decode_fwd: the size limits, the dtypes and
+ *   group sizes, d 64 or 128, and the workspace, which
  *   must hold attn_decode_workspace_bytes(B, H_q, H_kv,
  *   max_blocks * page_size, d) bytes.  block_table must be 4-byte aligned
  *   (ATTN_ERR_ALIGN) and non-NULL when B > 0 (ATTN_ERR_NULL).

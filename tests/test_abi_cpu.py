@@ -84,7 +84,8 @@ def test_prefill_empty_is_noop(lib):
 @pytest.mark.parametrize("kw,code", [
     (dict(q=NULL), 1), (dict(o=NULL), 1), (dict(k=NULL), 1),
     (dict(Sq=2), 2), (dict(Sq=0), 2), (dict(Hq=6, Hkv=4), 2), (dict(B=-3), 2),
-    (dict(dtype=attn.ATTN_F32), 3), (dict(d=32), 3), (dict(d=256), 3), (dict(Hq=6, Hkv=2), 3),
+    (dict(dtype=attn.ATTN_F32, d=96), 3), (dict(dtype=attn.ATTN_F32, d=256), 3), (dict(dtype=9), 3),
+    (dict(d=32), 3), (dict(d=256), 3), (dict(Hq=6, Hkv=2), 3),
     (dict(Hq=64, Hkv=2), 3),
     (dict(ws=NULL), 5), (dict(wsb=16), 5), (dict(ws=MIS), 4), (dict(k=MIS), 4),
     (dict(scale=-math.inf), 7), (dict(Skv=(1 << 23) + 1, d=128), 2),
@@ -102,7 +103,8 @@ def decode_noalloc(q=P, k=P, v=P, o=P, B=1, Hq=2, Hkv=2, Sq=1, Skv=8, d=64, caus
 @pytest.mark.parametrize("kw,code", [
     (dict(q=NULL), 1), (dict(o=NULL), 1), (dict(k=NULL), 1),
     (dict(Sq=2), 2), (dict(Hq=6, Hkv=4), 2), (dict(B=-3), 2),
-    (dict(dtype=attn.ATTN_F32), 3), (dict(d=32), 3), (dict(d=256), 3), (dict(Hq=6, Hkv=2), 3),
+    (dict(dtype=attn.ATTN_F32, d=96), 3), (dict(dtype=attn.ATTN_F32, d=256), 3), (dict(dtype=9), 3),
+    (dict(d=32), 3), (dict(d=256), 3), (dict(Hq=6, Hkv=2), 3),
     (dict(q=MIS), 4), (dict(scale=math.nan), 7),
     # partials beyond the static scratch: B*H_q chunked splits of (d + 1) floats
     (dict(B=2048, Hq=32, Hkv=32, Skv=4096, d=128), 5),
@@ -189,7 +191,8 @@ def decode_paged(q=P, kp=P, vp=P, o=P, B=2, Hq=4, Hkv=4, d=64, scale=0.125, tabl
     (dict(pages=0), 2), (dict(Hq=6, Hkv=4), 2), (dict(B=-1), 2),
     (dict(max_blocks=1 << 24, page=256), 2),                   # capacity beyond int32
     (dict(max_blocks=(1 << 16) + 1, page=128, d=128), 2),      # one head's rows beyond 2^31 bytes
-    (dict(dtype=attn.ATTN_F32), 3), (dict(d=96), 3), (dict(d=256), 3), (dict(Hq=6, Hkv=2), 3),
+    (dict(dtype=attn.ATTN_F32, d=96), 3), (dict(dtype=attn.ATTN_F32, d=256), 3), (dict(dtype=9), 3),
+    (dict(d=96), 3), (dict(d=256), 3), (dict(Hq=6, Hkv=2), 3),
     (dict(q=MIS), 4), (dict(kp=MIS), 4), (dict(table=ctypes.c_void_p(0x10002)), 4), (dict(ws=MIS), 4),
     (dict(ws=NULL), 5), (dict(wsb=16), 5),
     (dict(scale=math.nan), 7),
