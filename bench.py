@@ -213,6 +213,57 @@ def cpu_baseline(wl, seconds, inputs=None):
     }
 
 
+def sustained_clock(torch, fn, seconds=0.3, period=0.005):
+    """Graphics clock the GPU holds while `fn` runs back to back: about
+    `seconds` of calls are queued, and the driver's current-SCLK line
+    (`pp_dpm_sclk`, the entry marked '*') is read every `period` s until they
+    finish.  Context only (outside any timed region): the published MFMA
+    peak assumes 2.4 GHz.  None when the file is not readable or several
+    cards make it ambiguous."""
+    import glob
+    import re
+    files = glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk")
+    if len(files) != 1:
+        return None
+
+    def read():
+        try:
+            with open(files[0]) as f:
+                for line in f:
+                    if line.rstrip().endswith("*"):
+                        m = re.search(r"(\d+)\s*Mhz", line, re.IGNORECASE)
+                        return int(m.group(1)) if m else None
+        except OSError:
+            return None
+        return None
+
+    if read() is None:
+        return None
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    fn()
+    torch.cuda.synchronize()
+    per_call = max(time.perf_counter() - t0, 1e-5)
+    calls = max(1, int(seconds / per_call))
+    for _ in range(calls):
+        fn()
+    done = torch.cuda.Event()
+    done.record()
+    time.sleep(0.02)   # let the clock settle under the load
+    samples = []
+    while not done.query():
+        v = read()
+        if v is not None:
+            samples.append(v)
+        time.sleep(period)
+    torch.cuda.synchronize()
+    if not samples:
+        return None
+    samples.sort()
+    return {"median_mhz": samples[len(samples) // 2], "min_mhz": samples[0], "max_mhz": samples[-1],
+            "samples": len(samples)}
+
+
 def read_probe(torch, dev, gib=4):
     """Rate of a plain streaming-read kernel on this device (the grid-stride
     nontemporal reads of libattn_probe.so over `gib` GiB, best over a few
@@ -592,6 +643,15 @@ def main():
                 "kernels exceed it)",
         "decode_over_probe": round(gbps / probe["gbps"], 4),
     }
+    clk_p, clk_d = sustained_clock(torch, fp), sustained_clock(torch, fd)
+    if clk_p or clk_d:
+        out["context"]["sustained_sclk"] = {
+            "prefill": clk_p, "decode": clk_d,
+            "source": "pp_dpm_sclk sampled while each headline workload ran back to back, after the "
+                      "timed steps; the published MFMA peak assumes 2400 MHz"}
+        if clk_p:
+            out["context"]["prefill_frac_of_peak_at_sustained_clock"] = round(
+                tflops / (PEAK_BF16_TFLOPS * clk_p["median_mhz"] / 2400.0), 4)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds, inputs)
     print(json.dumps(out), flush=True)
