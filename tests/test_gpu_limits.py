@@ -1,0 +1,96 @@
+"""GPU parity at the boundary's size limit: one head's rows of K and V span
+up to 2^31 - 1 bytes (the kernels address rows inside a head with 32-bit byte
+offsets, buffer loads among them), so at d = 128 a cache of 8,388,607 keys
+(2 GiB of K and 2 GiB of V) is the largest accepted, and one more key is
+rejected on the host.
+
+At that size: the decode with one query head per KV head (split into 4096
+chunks) and with a query group (the balanced pass: 65,536 units of 128 keys),
+and a chunk of 32 new queries at the end of the cache (causal, bottom-right),
+each compared over its whole output with the fp64 oracle (the C evaluation,
+which reads the bf16 caches in place).  Inputs are seeded N(0,1) drawn on the
+device (4 GiB per tensor would take minutes on the host generator); the
+oracle gets the exact tensors the kernels read.
+"""
+import os
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import attention_attn_fwd_11_amd as attn
+import oracle
+from tests.gpu_util import assert_close
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+D = 128
+S_MAX = (2**31 - 1) // (D * 2)   # 8,388,607 keys
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    assert os.path.exists(attn.library_path), "libattn.so must be built before GPU tests"
+    torch.cuda.init()
+    yield
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+
+@pytest.fixture(scope="module")
+def cache():
+    g = torch.Generator(device=DEV).manual_seed(91)
+    k = torch.randn((1, 1, S_MAX, D), generator=g, device=DEV, dtype=torch.float32).to(torch.bfloat16)
+    v = torch.randn((1, 1, S_MAX, D), generator=g, device=DEV, dtype=torch.float32).to(torch.bfloat16)
+    torch.cuda.synchronize()
+    say(f"cache: K and V [1, 1, {S_MAX}, {D}] bf16, {k.numel() * 2 / 2**30:.2f} GiB each")
+    yield k, v, k.cpu(), v.cpu()
+    del k, v
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("Hq", [1, 2])
+def test_decode_at_the_head_size_limit(cache, Hq):
+    k, v, kc, vc = cache
+    say(f"decode at the limit: Hq {Hq}, Hkv 1, S_kv {S_MAX}")
+    g = torch.Generator(device=DEV).manual_seed(92 + Hq)
+    q = torch.randn((1, Hq, 1, D), generator=g, device=DEV, dtype=torch.float32).to(torch.bfloat16)
+    scale = 1.0 / np.sqrt(D)
+    o = attn.decode(q, k, v, scale=scale)
+    torch.cuda.synchronize()
+    ref = oracle.decode(q.cpu(), kc, vc, None, scale)
+    assert_close(o, ref, torch.bfloat16, f"decode Hq{Hq} S{S_MAX}")
+
+
+def test_prefill_chunk_at_the_head_size_limit(cache):
+    k, v, kc, vc = cache
+    Sq = 32
+    say(f"prefill at the limit: {Sq} queries at the end of {S_MAX} keys, causal")
+    g = torch.Generator(device=DEV).manual_seed(95)
+    q = torch.randn((1, 1, Sq, D), generator=g, device=DEV, dtype=torch.float32).to(torch.bfloat16)
+    scale = 1.0 / np.sqrt(D)
+    o = attn.prefill(q, k, v, causal=True, scale=scale)
+    torch.cuda.synchronize()
+    ref = oracle.attention(q.cpu(), kc, vc, True, scale)
+    assert_close(o, ref, torch.bfloat16, f"prefill Sq{Sq} S{S_MAX}")
+
+
+def test_one_key_past_the_limit_is_rejected():
+    """The host check refuses S_kv = S_MAX + 1 before touching the device
+    (no tensor of that size is needed: the C ABI sees only the sizes)."""
+    P = 1 << 12
+    assert attn.attn_decode_workspace_bytes(1, 1, 1, S_MAX + 1, D) > 0
+    st = attn.attn_decode_fwd(P, P, P, P, 1, 1, 1, 1, S_MAX + 1, D, 0, 0.1, None, attn.ATTN_BF16,
+                              P, 1 << 30, None)
+    assert st == 2, attn.STATUS.get(st)
+    st = attn.attn_prefill_fwd(P, P, P, P, 1, 1, 1, 32, S_MAX + 1, D, 1, 0.1, None, attn.ATTN_BF16, None)
+    assert st == 2, attn.STATUS.get(st)
