@@ -94,3 +94,28 @@ def test_one_key_past_the_limit_is_rejected():
     assert st == 2, attn.STATUS.get(st)
     st = attn.attn_prefill_fwd(P, P, P, P, 1, 1, 1, 32, S_MAX + 1, D, 1, 0.1, None, attn.ATTN_BF16, None)
     assert st == 2, attn.STATUS.get(st)
+
+
+@pytest.mark.parametrize("what", ["prefill_bf16_d256", "decode_f32_d128"])
+def test_512_byte_rows_at_the_head_size_limit(what):
+    """Rows of 512 bytes (bf16 at d = 256, fp32 at d = 128): 4,194,303 keys."""
+    d, dt = (256, torch.bfloat16) if what == "prefill_bf16_d256" else (128, torch.float32)
+    s_max = (2**31 - 1) // (d * (2 if dt == torch.bfloat16 else 4))
+    say(f"{what} at the limit: S_kv {s_max}")
+    g = torch.Generator(device=DEV).manual_seed(97)
+    k = torch.randn((1, 1, s_max, d), generator=g, device=DEV, dtype=torch.float32).to(dt)
+    v = torch.randn((1, 1, s_max, d), generator=g, device=DEV, dtype=torch.float32).to(dt)
+    scale = 1.0 / np.sqrt(d)
+    if what == "prefill_bf16_d256":
+        q = torch.randn((1, 1, 16, d), generator=g, device=DEV, dtype=torch.float32).to(dt)
+        o = attn.prefill(q, k, v, causal=True, scale=scale)
+        torch.cuda.synchronize()
+        ref = oracle.attention(q.cpu(), k.cpu(), v.cpu(), True, scale)
+    else:
+        q = torch.randn((1, 2, 1, d), generator=g, device=DEV, dtype=torch.float32)
+        o = attn.decode(q, k, v, scale=scale)
+        torch.cuda.synchronize()
+        ref = oracle.decode(q.cpu(), k.cpu(), v.cpu(), None, scale)
+    assert_close(o, ref, dt, f"{what} S{s_max}")
+    del k, v
+    torch.cuda.empty_cache()
