@@ -13,10 +13,16 @@
 //   decode_split_valu<D>     one query head per KV head (no reuse of K/V
 //                            across queries: a streaming dot product, so the
 //                            vector ALU is the right unit).
-//   decode_split_mfma<D, G>  G >= 2 query heads share each KV head: the G
-//                            queries form a small matrix and QK^T and PV run on
+//   decode_split_balanced<D, G>  G >= 2 query heads share each KV head, at
+//                            most 2048 sequences: the G queries form a small
+//                            matrix and QK^T and PV run on
 //                            v_mfma_f32_16x16x32_bf16 with the group padded to
-//                            16 rows.
+//                            16 columns; a persistent pass over equal units of
+//                            128 keys, with K and V staged per wave in LDS
+//                            and each wave's next copies in flight while it
+//                            computes.  decode_combine_balanced merges.
+//   decode_split_mfma<D, G>  the same contraction on a grid of (chunk, KV
+//                            head, batch) workgroups, for larger batches.
 //   decode_combine<D>        merges the partials of one (batch, query head);
 //                            not launched when every head has a single split
 //                            (decode_split_valu then writes O itself).
