@@ -1,5 +1,5 @@
 """Build libattn.so (the gfx950 kernels and the C ABI), libattn_probe.so
-(a streaming-read probe the benchmark uses for context) and
+(the streaming-read and matrix-core probes the benchmark uses for context) and
 libattn_lds_poison.so (the same library with every direct global -> LDS copy
 preceded by a NaN fill of its destination, a debug build the tests use to
 catch missing waits and barriers), with hipcc.

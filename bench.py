@@ -302,6 +302,53 @@ def read_probe(torch, dev, gib=4):
             "kernel": "grid-stride 16-byte nontemporal loads, 8 in flight per lane (libattn_probe.so)"}
 
 
+def mfma_probe(torch, dev, steps, warmup, iters=1024):
+    """Rate of back-to-back v_mfma_f32_32x32x16_bf16 from registers
+    (libattn_probe.so: two waves per SIMD, one workgroup per compute unit,
+    random bf16 operands), timed like the prefill: `warmup` untimed launches,
+    then `steps` launches each between HIP events on the current stream, one
+    launch lasting about as long as one headline prefill.  Context only: what
+    the matrix cores sustain, at the clock the chip holds under that load,
+    with no memory, LDS or vector work beside them.  The roofline peak is
+    the published 2516.6 TFLOP/s."""
+    import ctypes
+    lib = ctypes.CDLL(os.path.join(ROOT, "attention_attn_fwd_11_amd", "libattn_probe.so"))
+    lib.attn_probe_mfma.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
+                                    ctypes.c_void_p]
+    lib.attn_probe_mfma_operand_bytes.restype = ctypes.c_size_t
+    lib.attn_probe_mfma_flops.argtypes = [ctypes.c_int32, ctypes.c_int32]
+    lib.attn_probe_mfma_flops.restype = ctypes.c_double
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    g = torch.Generator().manual_seed(7)
+    ops = torch.randn(lib.attn_probe_mfma_operand_bytes() // 2, generator=g).to(torch.bfloat16).to(dev)
+    out = torch.empty(cus * 512, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream().cuda_stream
+
+    def launch():
+        rc = lib.attn_probe_mfma(ops.data_ptr(), out.data_ptr(), cus, iters, stream)
+        if rc != 0:
+            raise RuntimeError(f"matrix-core probe failed ({rc})")
+
+    for _ in range(warmup):
+        launch()
+    torch.cuda.synchronize()
+    tm = Timer(torch)
+    for _ in range(steps):
+        tm(launch)
+    torch.cuda.synchronize()
+    ms, _ = tm.mean_ms()
+    flops = lib.attn_probe_mfma_flops(cus, iters)
+    res = {"tflops": round(flops / (ms * 1e-3) / 1e12, 1), "ms": round(ms, 4), "workgroups": cus,
+           "flop_per_launch": flops,
+           "kernel": "v_mfma_f32_32x32x16_bf16 only, 4 independent accumulators per wave, 2 waves per SIMD "
+                     "(libattn_probe.so)"}
+    clk = sustained_clock(torch, launch)
+    if clk:
+        res["sustained_sclk"] = clk
+    del ops, out
+    return res
+
+
 def varlen_prefill(torch, attn, wl, dev, steps, warmup):
     """Packed causal prefill over sequences of mixed lengths (the varlen
     workload: q and k lengths equal, drawn from U[256, 4096])."""
@@ -643,6 +690,9 @@ def main():
                 "kernels exceed it)",
         "decode_over_probe": round(gbps / probe["gbps"], 4),
     }
+    mp = mfma_probe(torch, dev, args.steps, args.warmup)
+    out["context"]["mfma_probe"] = mp
+    out["context"]["prefill_frac_of_mfma_probe"] = round(tflops / mp["tflops"], 4)
     clk_p, clk_d = sustained_clock(torch, fp), sustained_clock(torch, fd)
     if clk_p or clk_d:
         out["context"]["sustained_sclk"] = {

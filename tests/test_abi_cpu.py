@@ -248,3 +248,33 @@ def test_cached_workspace_refused_under_graph_capture(monkeypatch):
     monkeypatch.setattr(torch.cuda, "is_current_stream_capturing", lambda: True)
     with pytest.raises(RuntimeError, match="workspace"):
         attn.workspace_for("cuda:0", 1024)
+
+
+def test_context_probe_library_exports_and_rejects():
+    """libattn_probe.so (measurement context only): every probe entry point
+    is exported and invalid arguments return 1 before any HIP call."""
+    path = os.path.join(ROOT, "attention_attn_fwd_11_amd", "libattn_probe.so")
+    if not os.path.exists(path):
+        pytest.skip("libattn_probe.so not built")
+    pl = ctypes.CDLL(path)
+    for n in ("attn_probe_stream_read", "attn_probe_out_words", "attn_probe_mfma",
+              "attn_probe_mfma_operand_bytes", "attn_probe_mfma_flops"):
+        assert hasattr(pl, n), n
+    pl.attn_probe_mfma.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
+                                   ctypes.c_void_p]
+    pl.attn_probe_mfma_operand_bytes.restype = ctypes.c_size_t
+    pl.attn_probe_mfma_flops.argtypes = [ctypes.c_int32, ctypes.c_int32]
+    pl.attn_probe_mfma_flops.restype = ctypes.c_double
+    assert pl.attn_probe_mfma_operand_bytes() == 2 * 4 * 64 * 16
+    # blocks x 8 waves x iters x 16 MFMAs x (2 x 32 x 32 x 16) FLOP
+    assert pl.attn_probe_mfma_flops(256, 1024) == 256 * 8 * 1024 * 16 * 32768
+    assert pl.attn_probe_mfma_flops(0, 5) == 0.0
+    assert pl.attn_probe_mfma(NULL, P, 1, 1, NULL) == 1
+    assert pl.attn_probe_mfma(P, NULL, 1, 1, NULL) == 1
+    assert pl.attn_probe_mfma(MIS, P, 1, 1, NULL) == 1
+    assert pl.attn_probe_mfma(P, P, 0, 1, NULL) == 1
+    assert pl.attn_probe_mfma(P, P, 1, 0, NULL) == 1
+    pl.attn_probe_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
+                                          ctypes.c_int32, ctypes.c_void_p]
+    assert pl.attn_probe_stream_read(P, 24, P, 1, NULL) == 1
+    assert pl.attn_probe_stream_read(MIS, 32, P, 1, NULL) == 1
