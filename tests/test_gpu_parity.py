@@ -136,6 +136,7 @@ DECODE_CASES = [
     (4, 8, 2, 700, 128, [700, 256, 255, 3]),
     (2, 16, 4, 600, 128, [600, 17]),
     (2, 32, 2, 600, 128, [599, 300]),
+    (3, 16, 2, 800, 128, [800, 431, 128]),
     (3, 3, 3, 900, 64, [900, 512, 1]),
     (3, 8, 1, 900, 64, [2, 900, 0]),
     (2, 4, 2, 64, 64, None),
