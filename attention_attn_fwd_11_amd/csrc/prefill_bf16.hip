@@ -9,10 +9,12 @@
 //
 // gfx950 design
 //   - 512 threads = 8 waves; each wave owns 32 query rows (256 per workgroup,
-//     one workgroup per CU at d = 128).  At d = 256: 256 threads, 4 waves
-//     (one per SIMD, so a wave may use 512 registers), 128 rows.  Large tiles halve the K/V traffic per query
-//     row against 128-row tiles; the eight waves (two per SIMD) hide each
-//     other's softmax behind their matrix work.
+//     one workgroup per CU at d = 128).  At d = 256 (only the rotary
+//     variants: d = 256 without rotation runs prefill_d256.hip): 256
+//     threads, 4 waves (one per SIMD, so a wave may use 512 registers), 128
+//     rows.  Large tiles halve the K/V traffic per query row against 128-row
+//     tiles; with two waves per SIMD one wave's matrix work runs while the
+//     other is in its softmax.
 //   - Scores are formed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16:
 //     K rows (from LDS) are the A operand and Q^T (held in registers for the
 //     whole loop) is the B operand.  In the accumulator each lane then holds
