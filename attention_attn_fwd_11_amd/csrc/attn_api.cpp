@@ -49,6 +49,11 @@ attn_status_t check_common(const void* q, const void* k, const void* v, const vo
   return ATTN_OK;
 }
 
+// The decode kernels and the fp32 prefill index batches and heads by the
+// grid's second and third dimensions, which the device limits to 65536.
+constexpr int32_t kMaxGridYZ = 65535;
+bool grid_yz_ok(int32_t B, int32_t H_q) { return B <= kMaxGridYZ && H_q <= kMaxGridYZ; }
+
 // Causal prefill: pair query tiles n_qt-1-p and p in one workgroup when the
 // queries span at least half of the keys (the tiles' work then grows along
 // the diagonal and the pairs even it out); a short chunk of queries at the
@@ -298,6 +303,7 @@ attn_status_t attn_prefill_fwd(const void* q, const void* k, const void* v, void
   attn_status_t st = check_common(q, k, v, o, B, H_q, H_kv, S_q, S_kv, d, causal, scale, dtype);
   if (st != ATTN_OK) return st;
   if (causal && S_q > S_kv) return ATTN_ERR_SHAPE;
+  if (dtype == ATTN_F32 && !grid_yz_ok(B, H_q)) return ATTN_ERR_SHAPE;
   if ((int64_t)B * S_q == 0) return ATTN_OK;  // nothing to compute
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (S_kv == 0) {
@@ -414,7 +420,7 @@ attn_status_t attn_decode_fwd(const void* q, const void* k_cache, const void* v_
   attn_status_t st = check_common(q, k_cache, v_cache, o, B, H_q, H_kv, S_q, S_kv, d, causal,
                                   scale, dtype);
   if (st != ATTN_OK) return st;
-  if (S_q != 1) return ATTN_ERR_SHAPE;
+  if (S_q != 1 || !grid_yz_ok(B, H_q)) return ATTN_ERR_SHAPE;
   return run_decode(q, k_cache, v_cache, o, B, H_q, H_kv, S_kv, d, scale, kv_lens, dtype, workspace,
                     workspace_bytes, stream, nullptr, 0, 0, 0);
 }
@@ -427,7 +433,7 @@ attn_status_t attn_decode_noalloc_fwd(const void* q, const void* k_cache, const 
   attn_status_t st = check_common(q, k_cache, v_cache, o, B, H_q, H_kv, S_q, S_kv, d, causal,
                                   scale, dtype);
   if (st != ATTN_OK) return st;
-  if (S_q != 1) return ATTN_ERR_SHAPE;
+  if (S_q != 1 || !grid_yz_ok(B, H_q)) return ATTN_ERR_SHAPE;
   if (!decode_supported(H_q, H_kv, d, dtype)) return ATTN_ERR_UNSUPPORTED;
   const size_t need = workspace_bytes(B, H_q, H_kv, S_kv, d);
   if (need > kScratchBytes) return ATTN_ERR_WORKSPACE;   // beyond the static scratch
@@ -455,6 +461,7 @@ attn_status_t attn_decode_paged_fwd(const void* q, const void* k_pages, const vo
   attn_status_t st = check_common(q, k_pages, v_pages, o, B, H_q, H_kv, 1, (int32_t)cap, d, 0,
                                   scale, dtype);
   if (st != ATTN_OK) return st;
+  if (!grid_yz_ok(B, H_q)) return ATTN_ERR_SHAPE;
   if (B > 0 && !block_table) return ATTN_ERR_NULL;
   if (reinterpret_cast<uintptr_t>(block_table) & 3u) return ATTN_ERR_ALIGN;
   return run_decode(q, k_pages, v_pages, o, B, H_q, H_kv, (int32_t)cap, d, scale, kv_lens, dtype,

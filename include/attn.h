@@ -73,8 +73,9 @@ typedef enum {
  *
  *   q [B,H_q,S_q,d], k/v [B,H_kv,S_kv,d], o [B,H_q,S_q,d]   (device, dtype)
  *   B >= 0, S_q >= 0, S_kv >= 0, H_q >= 1, H_kv >= 1, H_q % H_kv == 0.
- *   One head's rows (S_q*d or S_kv*d elements) span at most 2^31 - 1 bytes
- *   (else ATTN_ERR_SHAPE).
+ *   One head's rows (S_q*d or S_kv*d elements) span at most 2^31 - 1 bytes,
+ *   B*H_q <= 2^30 - 1, and with ATTN_F32 B <= 65535 and H_q <= 65535 (the
+ *   grid dimensions the kernel indexes them by); else ATTN_ERR_SHAPE.
  *   d: 64 or 128, and 256 with ATTN_BF16 (else ATTN_ERR_UNSUPPORTED).
  *   causal: 0 or 1; causal with S_q > S_kv is rejected (ATTN_ERR_SHAPE).
  *   scale: finite; the usual value is 1/sqrt(d).
@@ -166,8 +167,10 @@ attn_status_t attn_prefill_varlen_fwd(const void* q, const void* k, const void* 
  *   q [B,H_q,1,d], o [B,H_q,1,d]; k_cache/v_cache [B,H_kv,S_kv,d] where S_kv is
  *   the cache capacity (the row stride between heads); batch b attends to its
  *   first clamp(kv_lens[b], 0, S_kv) rows.
- *   S_q must be 1 (else ATTN_ERR_SHAPE).  causal is accepted and has no
- *   effect with one query row (the bottom-right mask then allows every key).
+ *   S_q must be 1, and B <= 65535 and H_q <= 65535 (the grid dimensions the
+ *   kernels index them by); else ATTN_ERR_SHAPE.  causal is accepted and
+ *   has no effect with one query row (the bottom-right mask then allows
+ *   every key).  Size limits otherwise as attn_prefill_fwd.
  *   d: 64 or 128.  dtype: ATTN_BF16 with H_q/H_kv in {1, 2, 4, 8, 16}, or
  *   ATTN_F32 with any H_q/H_kv (else ATTN_ERR_UNSUPPORTED); q, the caches and
  *   o all have that dtype.  bf16 computes scores and P V with fp32

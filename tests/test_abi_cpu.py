@@ -70,6 +70,9 @@ def decode(q=P, k=P, v=P, o=P, B=1, Hq=2, Hkv=2, Sq=1, Skv=8, d=64, causal=0, sc
     # one head's rows must span at most 2^31 - 1 bytes
     (dict(Skv=(1 << 23) + 1, d=128), 2), (dict(Sq=(1 << 23) + 1, Skv=(1 << 23) + 1, causal=0, d=128), 2),
     (dict(Skv=(1 << 22) + 1, d=128, dtype=attn.ATTN_F32), 2),
+    # B * H_q at most 2^30 - 1; fp32 indexes B and H_q by grid dimensions of at most 65535
+    (dict(B=1 << 15, Hq=1 << 15, Hkv=1 << 15), 2),
+    (dict(B=65536, Hq=1, Hkv=1, dtype=attn.ATTN_F32), 2), (dict(B=1, Hq=65536, Hkv=1, dtype=attn.ATTN_F32), 2),
 ])
 def test_prefill_rejects(lib, kw, code):
     assert prefill(**kw) == code
@@ -89,6 +92,9 @@ def test_prefill_empty_is_noop(lib):
     (dict(Hq=64, Hkv=2), 3),
     (dict(ws=NULL), 5), (dict(wsb=16), 5), (dict(ws=MIS), 4), (dict(k=MIS), 4),
     (dict(scale=-math.inf), 7), (dict(Skv=(1 << 23) + 1, d=128), 2),
+    # batches and query heads are grid dimensions of at most 65535
+    (dict(B=65536, Hq=1, Hkv=1), 2), (dict(B=1, Hq=65536, Hkv=65536), 2),
+    (dict(B=65536, Hq=1, Hkv=1, dtype=attn.ATTN_F32), 2),
 ])
 def test_decode_rejects(lib, kw, code):
     assert decode(**kw) == code
@@ -108,6 +114,7 @@ def decode_noalloc(q=P, k=P, v=P, o=P, B=1, Hq=2, Hkv=2, Sq=1, Skv=8, d=64, caus
     (dict(q=MIS), 4), (dict(scale=math.nan), 7),
     # partials beyond the static scratch: B*H_q chunked splits of (d + 1) floats
     (dict(B=2048, Hq=32, Hkv=32, Skv=4096, d=128), 5),
+    (dict(B=65536, Hq=1, Hkv=1), 2),
 ])
 def test_decode_noalloc_rejects(lib, kw, code):
     """The allocation-free decode validates on the host, before it looks up
@@ -196,6 +203,7 @@ def decode_paged(q=P, kp=P, vp=P, o=P, B=2, Hq=4, Hkv=4, d=64, scale=0.125, tabl
     (dict(q=MIS), 4), (dict(kp=MIS), 4), (dict(table=ctypes.c_void_p(0x10002)), 4), (dict(ws=MIS), 4),
     (dict(ws=NULL), 5), (dict(wsb=16), 5),
     (dict(scale=math.nan), 7),
+    (dict(B=65536, Hq=1, Hkv=1), 2),
 ])
 def test_decode_paged_rejects(lib, kw, code):
     assert decode_paged(**kw) == code
