@@ -119,11 +119,32 @@ def spread(ts):
     return {"median_ms": round(med, 4), "min_ms": round(s[0], 4), "max_ms": round(s[-1], 4)}
 
 
-def _oracle_rows(w, x, seconds, seed):
+def _errors(gpu, ref, dtype):
+    """Errors of a GPU result against the oracle's fp64 values, with the bar
+    the tests apply: bf16 max-abs <= 2e-2 and mean-abs <= 2e-3; fp32
+    norm-wise relative error <= 1e-5."""
+    import numpy as np
+    g = np.asarray(gpu, dtype=np.float64)
+    r = np.asarray(ref, dtype=np.float64)
+    e = np.abs(g - r)
+    out = {"elements": int(e.size), "max_abs": float(e.max()) if e.size else 0.0,
+           "mean_abs": float(e.mean()) if e.size else 0.0}
+    if dtype == "f32":
+        out["rel_norm"] = float(np.linalg.norm(g - r) / max(float(np.linalg.norm(r)), 1e-300))
+        out["pass"] = out["rel_norm"] <= 1e-5
+    else:
+        out["pass"] = out["max_abs"] <= 2e-2 and out["mean_abs"] <= 2e-3
+    for key in ("max_abs", "mean_abs", "rel_norm"):
+        if key in out:
+            out[key] = float(f"{out[key]:.3e}")
+    return out
+
+
+def _oracle_rows(w, x, seconds, seed, gpu_o=None):
     """Time the fp64 oracle (oracle.c, as it stands) on a growing sample of
     random (b, h, i) query rows of workload w until about `seconds` of wall
     time.  Returns (algorithmic FLOPs and K+V bytes of the rows done, seconds,
-    rows done)."""
+    rows done, errors of the GPU output gpu_o on those rows or None)."""
     import numpy as np
     import oracle
 
@@ -131,20 +152,25 @@ def _oracle_rows(w, x, seconds, seed):
     lens = x["kv_lens"].tolist()
     g = np.random.default_rng(seed)
     rows_done, keys, elapsed = 0, 0, 0.0
+    refs, gots = [], []
     batch = 16
     while elapsed < seconds:
         rows = np.stack([g.integers(0, w.B, batch), g.integers(0, w.Hq, batch),
                          g.integers(0, w.Sq, batch)], axis=1)
         t0 = time.perf_counter()
-        oracle.attention_rows(q, k, v, w.causal, w.scale, rows,
-                              kv_lens=lens if w.len_range else None)
+        ref = oracle.attention_rows(q, k, v, w.causal, w.scale, rows,
+                                    kv_lens=lens if w.len_range else None)
         elapsed += time.perf_counter() - t0
+        if gpu_o is not None:
+            refs.append(ref)
+            gots.append(gpu_o[rows[:, 0], rows[:, 1], rows[:, 2]].numpy())
         for b, _, i in rows.tolist():
             n = min(max(lens[b], 0), w.Skv)
             keys += max(0, min(n, i + n - w.Sq + 1)) if w.causal else n
         rows_done += batch
         batch = min(batch * 2, 4096)
-    return 4 * w.d * keys, 2 * 2 * w.d * keys, elapsed, rows_done
+    err = _errors(np.concatenate(gots), np.concatenate(refs), w.dtype) if refs else None
+    return 4 * w.d * keys, 2 * 2 * w.d * keys, elapsed, rows_done, err
 
 
 def cpu_baseline(wl, seconds, inputs=None):
@@ -153,7 +179,11 @@ def cpu_baseline(wl, seconds, inputs=None):
     per visible pair), GB/s for decode (K+V bytes of every visible row).
     The fp32 prefill and both decodes are evaluated in full; the two large
     prefills on random query rows, about `seconds` each.  The headline
-    prefill's entry is the top-level figure."""
+    prefill's entry is the top-level figure.  Where the GPU output of the
+    same inputs is at hand (the benchmark's last call), `parity` gives its
+    errors against the oracle's values just computed (the tests compare
+    every element of every configuration; this is the same check on what
+    the benchmark ran)."""
     import oracle
 
     per = {}
@@ -165,38 +195,44 @@ def cpu_baseline(wl, seconds, inputs=None):
             return {key: t.cpu() for key, t in inputs[w.name].items() if key != "o"}
         return wl.generate(w, "cpu")
 
+    def gpu_out(w):
+        o = inputs.get(w.name, {}).get("o")
+        return None if o is None else o.float().cpu()
+
     def full(w, reps_seconds=0.5):
         x = host(w)
         lens = x["kv_lens"]
         n, t = 0, 0.0
         while t < reps_seconds or n == 0:
             t0 = time.perf_counter()
-            oracle.attention(x["q"], x["k"], x["v"], w.causal, w.scale,
-                             kv_lens=lens if (w.len_range or w.kind == "decode") else None)
+            ref = oracle.attention(x["q"], x["k"], x["v"], w.causal, w.scale,
+                                   kv_lens=lens if (w.len_range or w.kind == "decode") else None)
             t += time.perf_counter() - t0
             n += 1
-        return x, t / n
+        o = gpu_out(w)
+        err = None if o is None else _errors(o.numpy(), ref, w.dtype)
+        return x, t / n, err
 
     w1 = wl.BY_NAME["prefill_f32_small"]
-    _, t1 = full(w1)
+    _, t1, e1 = full(w1)
     f1 = wl.prefill_flops(w1)
     per[w1.name] = {"value": f1 / t1 / 1e9, "unit": "GFLOP/s", "seconds_per_call": t1,
-                    "sample": "whole output (fp32 inputs)"}
+                    "sample": "whole output (fp32 inputs)", "parity": e1}
     for name in ("decode_bf16_b64h32l4096", "decode_gqa_bf16_b128h32kv8"):
         w = wl.BY_NAME[name]
-        x, t = full(w, 0.0)
+        x, t, err = full(w, 0.0)
         by = wl.decode_kv_bytes(w, x["kv_lens"])
         per[name] = {"value": by / t / 1e9, "unit": "GB/s", "seconds_per_call": t,
-                     "sample": "whole output"}
+                     "sample": "whole output", "parity": err}
     for name in ("prefill_bf16_b4h32s4096", "prefill_gqa_bf16_h64kv8s16384"):
         w = wl.BY_NAME[name]
         x = host(w)
-        fl, _, t, rows = _oracle_rows(w, x, seconds, seed=0)
+        fl, _, t, rows, err = _oracle_rows(w, x, seconds, seed=0, gpu_o=gpu_out(w))
         full_fl = wl.prefill_flops(w)
         per[name] = {"value": fl / t / 1e12, "unit": "TFLOP/s",
                      "seconds_whole_call_est": full_fl / (fl / t),
                      "sample": f"{rows} random (b, h, i) query rows ({fl / 1e9:.1f} GFLOP fp64, "
-                               f"{t:.1f} s)"}
+                               f"{t:.1f} s)", "parity": err}
     for rec in per.values():
         rec["value"] = round(rec["value"], 6 if rec["unit"] == "TFLOP/s" else 3)
         for key in ("seconds_per_call", "seconds_whole_call_est"):
@@ -402,12 +438,15 @@ def rope_prefill(torch, attn, wl, x, w, steps, warmup):
                     "kernel (ms covers both launches)", **res}
 
 
-def f32_small(torch, attn, wl, dev, steps, warmup):
+def f32_small(torch, attn, wl, dev, steps, warmup, inputs=None):
     """The fp32 causal prefill B1 H2 S128 d64 (parity-sized; latency-bound, so
-    its time is reported without a roofline fraction)."""
+    its time is reported without a roofline fraction).  Its tensors and
+    output are added to `inputs`."""
     w = wl.BY_NAME["prefill_f32_small"]
     x = wl.generate(w, dev)
     out = torch.empty_like(x["q"])
+    if inputs is not None:
+        inputs[w.name] = {**x, "o": out}
     f = lambda: attn.prefill(x["q"], x["k"], x["v"], causal=True, scale=w.scale, out=out)
     for _ in range(warmup):
         f()
@@ -682,7 +721,7 @@ def main():
         other["prefill_rope_bf16_b4h32s4096"] = rope_prefill(torch, attn, wl, inputs[wp.name], wp,
                                                              args.steps, args.warmup)
     other["decode_graph_small"] = decode_graph(torch, attn, wl, dev)
-    other["prefill_f32_small"] = f32_small(torch, attn, wl, dev, args.steps, args.warmup)
+    other["prefill_f32_small"] = f32_small(torch, attn, wl, dev, args.steps, args.warmup, inputs)
     probe = read_probe(torch, dev)
     out["context"] = {
         "streaming_read_probe": probe,
@@ -690,6 +729,12 @@ def main():
                 "kernels exceed it)",
         "decode_over_probe": round(gbps / probe["gbps"], 4),
     }
+    props = torch.cuda.get_device_properties(dev)
+    out["context"]["device"] = {
+        "name": props.name, "arch": getattr(props, "gcnArchName", None),
+        "compute_units": props.multi_processor_count,
+        "memory_gib": round(props.total_memory / 2**30, 1),
+        "hip": getattr(torch.version, "hip", None), "torch": torch.__version__}
     mp = mfma_probe(torch, dev, args.steps, args.warmup)
     out["context"]["mfma_probe"] = mp
     out["context"]["prefill_frac_of_mfma_probe"] = round(tflops / mp["tflops"], 4)
