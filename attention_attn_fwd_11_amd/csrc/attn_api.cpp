@@ -63,12 +63,20 @@ int pair_tiles(int32_t causal, int32_t S_q, int32_t S_kv) {
   return causal && 2LL * S_q >= S_kv ? 1 : 0;
 }
 
-// Decode work decomposition.  Query groups (G >= 2) with at most
+// bf16 query groups the matrix-core decode kernels take; the others (and
+// one query head per KV head) run the vector-ALU split kernel per query head.
+bool mfma_group(int32_t H_q, int32_t H_kv) {
+  const int G = H_q / H_kv;
+  return G == 2 || G == 4 || G == 8 || G == 16;
+}
+
+// Decode work decomposition.  Matrix-core query groups with at most
 // kDecodeMaxBatch sequences use the balanced pass: fixed units of
 // kDecodeUnit keys spread evenly over a persistent grid.  Otherwise the cache
-// is split into equal chunks per (batch, head).
+// is split into equal chunks per (batch, head): KV head for the matrix-core
+// kernels, query head for the vector-ALU one.
 bool decode_balanced(int32_t B, int32_t H_q, int32_t H_kv) {
-  return H_q / H_kv >= 2 && B <= attn::kDecodeMaxBatch;
+  return mfma_group(H_q, H_kv) && B <= attn::kDecodeMaxBatch;
 }
 
 // Keys per split (or per unit on the balanced pass).  Test-only override for
@@ -85,7 +93,7 @@ int decode_chunk(int32_t B, int32_t H_q, int32_t H_kv, int32_t S_kv) {
   // 512 keys: each split costs a partial (d+1 floats) per query.  (For B64
   // H32 L4096 one split per head would stream at 6.95 TB/s, two, as chosen,
   // at 6.86, four at 6.75.)
-  const int64_t heads = (int64_t)B * H_kv;
+  const int64_t heads = (int64_t)B * (mfma_group(H_q, H_kv) ? H_kv : H_q);
   int64_t splits = heads >= 4096 ? 1 : (4096 + heads - 1) / heads;
   const int64_t max_splits = (S_kv + 511) / 512;
   if (splits > max_splits) splits = max_splits;
@@ -138,13 +146,13 @@ size_t workspace_bytes(int32_t B, int32_t H_q, int32_t H_kv, int32_t S_kv, int32
   return round_up(rows * d * sizeof(float), 256) + round_up(rows * sizeof(float), 256);
 }
 
-// What the decode kernels implement: d 64 or 128; bf16 with query groups of
-// 1, 2, 4, 8 or 16 heads, fp32 with any group size.
+// What the decode kernels implement: d 64 or 128, bf16 or fp32, any group
+// size.
 bool decode_supported(int32_t H_q, int32_t H_kv, int32_t d, attn_dtype_t dtype) {
-  const int G = H_q / H_kv;
+  (void)H_q;
+  (void)H_kv;
   if (d != 64 && d != 128) return false;
-  if (dtype == ATTN_F32) return true;
-  return dtype == ATTN_BF16 && (G == 1 || G == 2 || G == 4 || G == 8 || G == 16);
+  return dtype == ATTN_F32 || dtype == ATTN_BF16;
 }
 
 // Scratch of the allocation-free decode entry point (attn_decode_noalloc_fwd):

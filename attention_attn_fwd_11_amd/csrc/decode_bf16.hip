@@ -10,9 +10,14 @@
 // rescaling identity of that page's section 3.4 loop.
 //
 // Kernels
-//   decode_split_valu<D>     one query head per KV head (no reuse of K/V
-//                            across queries: a streaming dot product, so the
-//                            vector ALU is the right unit).
+//   decode_split_valu<D>     one workgroup per (chunk, query head, batch): a
+//                            streaming dot product on the vector ALU.  With
+//                            one query head per KV head there is no reuse of
+//                            K/V across queries, so this is the right unit;
+//                            it also serves the group sizes the matrix-core
+//                            kernels do not take (3, 5, 6, 7, 9-15, above
+//                            16), each query head streaming its KV head's
+//                            rows (the repeats are served mostly by cache).
 //   decode_split_balanced<D, G>  G >= 2 query heads share each KV head, at
 //                            most 2048 sequences: the G queries form a small
 //                            matrix and QK^T and PV run on
@@ -178,7 +183,8 @@ struct WaveMerge {
 };
 
 // ---------------------------------------------------------------------------
-// G = 1: vector-ALU split kernel.
+// Vector-ALU split kernel: one query head per workgroup (query head h reads
+// KV head h / (H_q / H_kv)).
 //
 // Lane layout: a key row is D/8 16-byte pieces; LPK = D/8 lanes cover one key
 // and a wave load instruction covers KPI = 64/LPK consecutive keys (1 KiB,
@@ -187,7 +193,11 @@ struct WaveMerge {
 // the LPK lanes of a key with a halving exchange, which leaves every key's
 // full score in one lane (pair).
 // ---------------------------------------------------------------------------
-template <int D>
+// STREAM (one query head per KV head): K and V are read with the nontemporal
+// hint, each byte once.  Otherwise (groups the matrix-core kernels do not
+// take) the query heads of a group each read their KV head's rows with
+// ordinary loads, so the repeats may still hit in cache.
+template <int D, bool STREAM>
 __global__ __launch_bounds__(kThreads) void decode_split_valu(DecodeParams p) {
   constexpr int LPK = D / 8;          // lanes per key row
   constexpr int KPI = 64 / LPK;       // keys per load instruction
@@ -197,6 +207,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_valu(DecodeParams p) {
   __shared__ WaveMerge<D> merge;
 
   const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int hk = STREAM ? h : h / (p.Hq / p.Hkv);   // its KV head
   int n = p.Skv;
   if (p.kv_lens) n = min(max(p.kv_lens[b], 0), p.Skv);
   const int c0 = split * p.chunk;
@@ -223,18 +234,18 @@ __global__ __launch_bounds__(kThreads) void decode_split_valu(DecodeParams p) {
   for (int e = 0; e < 8; ++e) o[e] = 0.f;
 
   for (int base = c0 + wave * KB; base < c1; base += kWaves * KB) {
-    const uint16_t* kp = kv_row<D>(p.k, p, b, h, base);   // rows base .. base+KB-1
-    const uint16_t* vp = kv_row<D>(p.v, p, b, h, base);
+    const uint16_t* kp = kv_row<D>(p.k, p, b, hk, base);   // rows base .. base+KB-1
+    const uint16_t* vp = kv_row<D>(p.v, p, b, hk, base);
     u32x4 kr[8], vr[8];
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       const int key = min(base + u * KPI + kg, c1 - 1) - base;
-      kr[u] = ld16_stream(kp + key * D + 8 * dc);
+      kr[u] = STREAM ? ld16_stream(kp + key * D + 8 * dc) : ld16(kp + key * D + 8 * dc);
     }
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       const int key = min(base + u * KPI + kg, c1 - 1) - base;
-      vr[u] = ld16_stream(vp + key * D + 8 * dc);
+      vr[u] = STREAM ? ld16_stream(vp + key * D + 8 * dc) : ld16(vp + key * D + 8 * dc);
     }
     // partial dots over this lane's 8 features
     float part[8];
@@ -943,9 +954,15 @@ hipError_t launch_d(const DecodeParams& p, hipStream_t stream) {
       default: return hipErrorInvalidValue;
     }
   }
-  dim3 grid(p.n_split, p.Hkv, p.B);
-  switch (G) {
-    case 1: hipLaunchKernelGGL((decode_split_valu<D>), grid, dim3(kThreads), 0, stream, p); break;
+  // Matrix cores for groups of 2, 4, 8, 16 (grid over KV heads); the
+  // vector-ALU kernel for every other group size (grid over query heads).
+  const bool mfma = G == 2 || G == 4 || G == 8 || G == 16;
+  const dim3 grid(p.n_split, mfma ? p.Hkv : p.Hq, p.B);
+  switch (mfma ? G : 1) {
+    case 1:
+      if (G == 1) hipLaunchKernelGGL((decode_split_valu<D, true>), grid, dim3(kThreads), 0, stream, p);
+      else hipLaunchKernelGGL((decode_split_valu<D, false>), grid, dim3(kThreads), 0, stream, p);
+      break;
     case 2: hipLaunchKernelGGL((decode_split_mfma<D, 2>), grid, dim3(kThreads), 0, stream, p); break;
     case 4: hipLaunchKernelGGL((decode_split_mfma<D, 4>), grid, dim3(kThreads), 0, stream, p); break;
     case 8: hipLaunchKernelGGL((decode_split_mfma<D, 8>), grid, dim3(kThreads), 0, stream, p); break;
@@ -954,7 +971,7 @@ hipError_t launch_d(const DecodeParams& p, hipStream_t stream) {
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if (G == 1 && p.n_split == 1) return hipSuccess;   // the split pass wrote O
+  if (!mfma && p.n_split == 1) return hipSuccess;   // the split pass wrote O
   hipLaunchKernelGGL((decode_combine<D>), dim3(p.Hq, p.B), dim3(64), 0, stream, p);
   return hipGetLastError();
 }

@@ -88,8 +88,7 @@ def test_prefill_empty_is_noop(lib):
     (dict(q=NULL), 1), (dict(o=NULL), 1), (dict(k=NULL), 1),
     (dict(Sq=2), 2), (dict(Sq=0), 2), (dict(Hq=6, Hkv=4), 2), (dict(B=-3), 2),
     (dict(dtype=attn.ATTN_F32, d=96), 3), (dict(dtype=attn.ATTN_F32, d=256), 3), (dict(dtype=9), 3),
-    (dict(d=32), 3), (dict(d=256), 3), (dict(Hq=6, Hkv=2), 3),
-    (dict(Hq=64, Hkv=2), 3),
+    (dict(d=32), 3), (dict(d=256), 3),
     (dict(ws=NULL), 5), (dict(wsb=16), 5), (dict(ws=MIS), 4), (dict(k=MIS), 4),
     (dict(scale=-math.inf), 7), (dict(Skv=(1 << 23) + 1, d=128), 2),
     # batches and query heads are grid dimensions of at most 65535
@@ -110,7 +109,7 @@ def decode_noalloc(q=P, k=P, v=P, o=P, B=1, Hq=2, Hkv=2, Sq=1, Skv=8, d=64, caus
     (dict(q=NULL), 1), (dict(o=NULL), 1), (dict(k=NULL), 1),
     (dict(Sq=2), 2), (dict(Hq=6, Hkv=4), 2), (dict(B=-3), 2),
     (dict(dtype=attn.ATTN_F32, d=96), 3), (dict(dtype=attn.ATTN_F32, d=256), 3), (dict(dtype=9), 3),
-    (dict(d=32), 3), (dict(d=256), 3), (dict(Hq=6, Hkv=2), 3),
+    (dict(d=32), 3), (dict(d=256), 3),
     (dict(q=MIS), 4), (dict(scale=math.nan), 7),
     # partials beyond the static scratch: B*H_q chunked splits of (d + 1) floats
     (dict(B=2048, Hq=32, Hkv=32, Skv=4096, d=128), 5),
@@ -199,7 +198,7 @@ def decode_paged(q=P, kp=P, vp=P, o=P, B=2, Hq=4, Hkv=4, d=64, scale=0.125, tabl
     (dict(max_blocks=1 << 24, page=256), 2),                   # capacity beyond int32
     (dict(max_blocks=(1 << 16) + 1, page=128, d=128), 2),      # one head's rows beyond 2^31 bytes
     (dict(dtype=attn.ATTN_F32, d=96), 3), (dict(dtype=attn.ATTN_F32, d=256), 3), (dict(dtype=9), 3),
-    (dict(d=96), 3), (dict(d=256), 3), (dict(Hq=6, Hkv=2), 3),
+    (dict(d=96), 3), (dict(d=256), 3),
     (dict(q=MIS), 4), (dict(kp=MIS), 4), (dict(table=ctypes.c_void_p(0x10002)), 4), (dict(ws=MIS), 4),
     (dict(ws=NULL), 5), (dict(wsb=16), 5),
     (dict(scale=math.nan), 7),
@@ -223,6 +222,20 @@ def test_workspace_bytes(lib):
     # grows with heads and capacity; covers at least one partial per query head
     assert ws(64, 32, 32, 8192, 128) >= a
     assert ws(2, 4, 1, 100, 64) >= 2 * 4 * (64 + 1) * 4
+
+
+def test_workspace_other_group_sizes(lib, monkeypatch):
+    """Group sizes the matrix-core kernels do not take (7, 32, 3) run the
+    vector-ALU split per query head: a partial per split and query head,
+    the split count aiming at about 4096 workgroups of (split, query head,
+    batch) and never below 512 keys per split."""
+    ws = attn.attn_decode_workspace_bytes
+    # B2 H_q28 H_kv4: 56 query heads -> 8 splits of 512 keys for 4096 keys
+    assert ws(2, 28, 4, 4096, 128) >= 2 * 28 * 8 * (128 + 1) * 4
+    # B4 H_q32 H_kv1 (one KV head): 128 query heads -> 4 splits of 512 for 2048 keys
+    assert ws(4, 32, 1, 2048, 64) >= 4 * 32 * 4 * (64 + 1) * 4
+    monkeypatch.setenv("ATTN_DECODE_CHUNK", "256")
+    assert ws(1, 3, 1, 1024, 128) >= 1 * 3 * 4 * (128 + 1) * 4
 
 
 def test_workspace_follows_chunk_override(lib, monkeypatch):

@@ -25,6 +25,8 @@ CASES = [
     (2, 8, 1, 512, 64, 128, [512, 300]),                   # d = 64, groups of 8
     (5, 4, 4, 1000, 64, 384, [1000, 999, 385, 384, 17]),   # page size 3 x 128, ragged capacity
     (3, 4, 2, 768, 64, 128, [768, 200, 1]),                # d = 64, groups of 2, a one-key cache
+    (2, 12, 4, 1280, 128, 256, [1280, 511]),               # groups of 3: vector-ALU pass per query head
+    (2, 32, 1, 640, 64, 128, [640, 129]),                  # one KV head for 32 query heads
 ]
 
 

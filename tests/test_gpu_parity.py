@@ -145,6 +145,13 @@ DECODE_CASES = [
     # one split per head (capacity <= 512): the split pass writes O itself
     (4, 2, 2, 500, 128, [500, 1, 0, 257]),
     (2, 3, 3, 512, 64, [512, 77]),
+    # group sizes the matrix-core kernels do not take: the vector-ALU pass per
+    # query head (3, 5, 7, one KV head for 32 query heads; split and unsplit)
+    (2, 6, 2, 900, 128, [900, 333]),
+    (2, 20, 4, 1300, 128, None),
+    (3, 7, 1, 700, 64, [700, 1, 256]),
+    (2, 32, 1, 1500, 128, [1500, 1024]),
+    (4, 6, 2, 500, 128, [500, 0, 1, 257]),
 ]
 
 
