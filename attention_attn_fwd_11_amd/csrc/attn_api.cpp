@@ -63,12 +63,24 @@ int pair_tiles(int32_t causal, int32_t S_q, int32_t S_kv) {
   return causal && 2LL * S_q >= S_kv ? 1 : 0;
 }
 
-// bf16 query groups the matrix-core decode kernels take; the others (and
-// one query head per KV head) run the vector-ALU split kernel per query head.
-bool mfma_group(int32_t H_q, int32_t H_kv) {
+// Query groups (G = H_q / H_kv >= 2) run on the matrix cores in column
+// blocks of at most 16 query heads: *blocks per KV head and *cb query heads
+// per block (the last block of a head may hold fewer).  One block of G for
+// G <= 16.
+void group_blocks(int32_t H_q, int32_t H_kv, int* blocks, int* cb) {
   const int G = H_q / H_kv;
-  return G == 2 || G == 4 || G == 8 || G == 16;
+  *blocks = (G + 15) / 16;
+  *cb = (G + *blocks - 1) / *blocks;
 }
+
+// Virtual KV heads of the matrix-core pass (H_kv times the blocks per head).
+int64_t virtual_heads(int32_t H_q, int32_t H_kv) {
+  int blocks = 1, cb = 1;
+  group_blocks(H_q, H_kv, &blocks, &cb);
+  return (int64_t)H_kv * blocks;
+}
+
+bool mfma_group(int32_t H_q, int32_t H_kv) { return H_q / H_kv >= 2; }
 
 // Decode work decomposition.  Matrix-core query groups with at most
 // kDecodeMaxBatch sequences use the balanced pass: fixed units of
@@ -93,7 +105,7 @@ int decode_chunk(int32_t B, int32_t H_q, int32_t H_kv, int32_t S_kv) {
   // 512 keys: each split costs a partial (d+1 floats) per query.  (For B64
   // H32 L4096 one split per head would stream at 6.95 TB/s, two, as chosen,
   // at 6.86, four at 6.75.)
-  const int64_t heads = (int64_t)B * (mfma_group(H_q, H_kv) ? H_kv : H_q);
+  const int64_t heads = (int64_t)B * (mfma_group(H_q, H_kv) ? virtual_heads(H_q, H_kv) : H_q);
   int64_t splits = heads >= 4096 ? 1 : (4096 + heads - 1) / heads;
   const int64_t max_splits = (S_kv + 511) / 512;
   if (splits > max_splits) splits = max_splits;
@@ -130,11 +142,15 @@ size_t partial_rows(int32_t B, int32_t H_q, int32_t H_kv, int32_t S_kv) {
   const int chunk = decode_chunk(B, H_q, H_kv, S_kv);
   const int64_t n_split = (S_kv + chunk - 1) / chunk;
   if (decode_balanced(B, H_q, H_kv)) {
-    // a run per (head, workgroup range) boundary: fewer than B*H_kv + n_wg,
-    // with n_wg at most kDecodeMaxWg and at most the number of units
-    int64_t wg = (int64_t)B * H_kv * n_split;
+    // a run per (virtual head, workgroup range) boundary: fewer than
+    // B*Hv + n_wg, with n_wg at most kDecodeMaxWg and at most the number of
+    // units; cb partial rows per run
+    int blocks = 1, cb = 1;
+    group_blocks(H_q, H_kv, &blocks, &cb);
+    const int64_t hv = (int64_t)H_kv * blocks;
+    int64_t wg = (int64_t)B * hv * n_split;
     if (wg > attn::kDecodeMaxWg) wg = attn::kDecodeMaxWg;
-    return (size_t)((int64_t)B * H_kv + wg) * (H_q / H_kv);
+    return (size_t)((int64_t)B * hv + wg) * cb;
   }
   return (size_t)B * H_q * n_split;
 }
@@ -247,6 +263,8 @@ attn_status_t run_decode(const void* q, const void* k, const void* v, void* o, i
   p.chunk = decode_chunk(B, H_q, H_kv, S_kv);
   p.n_split = (S_kv + p.chunk - 1) / p.chunk;
   p.n_wg = 0;
+  group_blocks(H_q, H_kv, &p.kv_div, &p.cb);
+  p.Hv = H_kv * p.kv_div;
   if (decode_balanced(B, H_q, H_kv)) {
     // Persistent grid: kDecodeWgPerCu workgroups per compute unit (the
     // resident capacity), never more than there are units.  The contiguous and the paged cache use the same
@@ -260,7 +278,7 @@ attn_status_t run_decode(const void* q, const void* k, const void* v, void* o, i
       const long w = std::strtol(env, nullptr, 10);
       if (w >= 1 && w <= (1 << 20)) wg = w;
     }
-    const int64_t max_units = (int64_t)B * H_kv * p.n_split;
+    const int64_t max_units = (int64_t)B * p.Hv * p.n_split;
     if (wg > max_units) wg = max_units;
     if (wg > attn::kDecodeMaxWg) wg = attn::kDecodeMaxWg;
     p.n_wg = (int)wg;

@@ -10,24 +10,24 @@
 // rescaling identity of that page's section 3.4 loop.
 //
 // Kernels
-//   decode_split_valu<D>     one workgroup per (chunk, query head, batch): a
-//                            streaming dot product on the vector ALU.  With
-//                            one query head per KV head there is no reuse of
-//                            K/V across queries, so this is the right unit;
-//                            it also serves the group sizes the matrix-core
-//                            kernels do not take (3, 5, 6, 7, 9-15, above
-//                            16), each query head streaming its KV head's
-//                            rows (the repeats are served mostly by cache).
-//   decode_split_balanced<D, G>  G >= 2 query heads share each KV head, at
-//                            most 2048 sequences: the G queries form a small
-//                            matrix and QK^T and PV run on
+//   decode_split_valu<D>     one query head per KV head (no reuse of K/V
+//                            across queries: a streaming dot product, so the
+//                            vector ALU is the right unit).
+//   decode_split_balanced<D, G, EXACT>  G >= 2 query heads share each KV
+//                            head, at most 2048 sequences: the queries form a
+//                            small matrix and QK^T and PV run on
 //                            v_mfma_f32_16x16x32_bf16 with the group padded to
 //                            16 columns; a persistent pass over equal units of
 //                            128 keys, with K and V staged per wave in LDS
 //                            and each wave's next copies in flight while it
 //                            computes.  decode_combine_balanced merges.
-//   decode_split_mfma<D, G>  the same contraction on a grid of (chunk, KV
-//                            head, batch) workgroups, for larger batches.
+//   decode_split_mfma<D, G, EXACT>  the same contraction on a grid of
+//                            (chunk, KV head, batch) workgroups, for larger
+//                            batches.
+//   EXACT: groups of exactly G = 2, 4, 8 or 16 query heads.  Otherwise any
+//   group size: each KV head's group is cut into column blocks of at most 16
+//   query heads (virtual KV heads, see GroupMap), each reading the KV head
+//   once, and G is the padded capacity (4, 8 or 16) of a block.
 //   decode_combine<D>        merges the partials of one (batch, query head);
 //                            not launched when every head has a single split
 //                            (decode_split_valu then writes O itself).
@@ -183,8 +183,7 @@ struct WaveMerge {
 };
 
 // ---------------------------------------------------------------------------
-// Vector-ALU split kernel: one query head per workgroup (query head h reads
-// KV head h / (H_q / H_kv)).
+// G = 1: vector-ALU split kernel.
 //
 // Lane layout: a key row is D/8 16-byte pieces; LPK = D/8 lanes cover one key
 // and a wave load instruction covers KPI = 64/LPK consecutive keys (1 KiB,
@@ -193,11 +192,7 @@ struct WaveMerge {
 // the LPK lanes of a key with a halving exchange, which leaves every key's
 // full score in one lane (pair).
 // ---------------------------------------------------------------------------
-// STREAM (one query head per KV head): K and V are read with the nontemporal
-// hint, each byte once.  Otherwise (groups the matrix-core kernels do not
-// take) the query heads of a group each read their KV head's rows with
-// ordinary loads, so the repeats may still hit in cache.
-template <int D, bool STREAM>
+template <int D>
 __global__ __launch_bounds__(kThreads) void decode_split_valu(DecodeParams p) {
   constexpr int LPK = D / 8;          // lanes per key row
   constexpr int KPI = 64 / LPK;       // keys per load instruction
@@ -207,7 +202,6 @@ __global__ __launch_bounds__(kThreads) void decode_split_valu(DecodeParams p) {
   __shared__ WaveMerge<D> merge;
 
   const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
-  const int hk = STREAM ? h : h / (p.Hq / p.Hkv);   // its KV head
   int n = p.Skv;
   if (p.kv_lens) n = min(max(p.kv_lens[b], 0), p.Skv);
   const int c0 = split * p.chunk;
@@ -234,18 +228,18 @@ __global__ __launch_bounds__(kThreads) void decode_split_valu(DecodeParams p) {
   for (int e = 0; e < 8; ++e) o[e] = 0.f;
 
   for (int base = c0 + wave * KB; base < c1; base += kWaves * KB) {
-    const uint16_t* kp = kv_row<D>(p.k, p, b, hk, base);   // rows base .. base+KB-1
-    const uint16_t* vp = kv_row<D>(p.v, p, b, hk, base);
+    const uint16_t* kp = kv_row<D>(p.k, p, b, h, base);   // rows base .. base+KB-1
+    const uint16_t* vp = kv_row<D>(p.v, p, b, h, base);
     u32x4 kr[8], vr[8];
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       const int key = min(base + u * KPI + kg, c1 - 1) - base;
-      kr[u] = STREAM ? ld16_stream(kp + key * D + 8 * dc) : ld16(kp + key * D + 8 * dc);
+      kr[u] = ld16_stream(kp + key * D + 8 * dc);
     }
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       const int key = min(base + u * KPI + kg, c1 - 1) - base;
-      vr[u] = STREAM ? ld16_stream(vp + key * D + 8 * dc) : ld16(vp + key * D + 8 * dc);
+      vr[u] = ld16_stream(vp + key * D + 8 * dc);
     }
     // partial dots over this lane's 8 features
     float part[8];
@@ -351,6 +345,27 @@ __global__ __launch_bounds__(kThreads) void decode_split_valu(DecodeParams p) {
   }
 }
 
+// Query columns of virtual KV head vh: the KV head it reads, its first
+// query head within the batch, and how many query heads it holds.  EXACT:
+// groups of exactly G, one block per KV head.
+template <int G, bool EXACT>
+struct GroupMap {
+  int hk, q0, g;
+  __device__ __forceinline__ GroupMap(const DecodeParams& p, int vh) {
+    if constexpr (EXACT) {
+      hk = vh;
+      q0 = vh * G;
+      g = G;
+    } else {
+      hk = vh / p.kv_div;
+      const int blk = vh - hk * p.kv_div;
+      const int grp = p.Hq / p.Hkv;
+      q0 = hk * grp + blk * p.cb;
+      g = min(p.cb, grp - blk * p.cb);
+    }
+  }
+};
+
 // ---------------------------------------------------------------------------
 // G >= 2: matrix-core split kernel.
 //
@@ -364,7 +379,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_valu(DecodeParams p) {
 // reads V^T with the LDS transpose read, so no workgroup barrier is needed
 // inside the loop.
 // ---------------------------------------------------------------------------
-template <int D, int G>
+template <int D, int G, bool EXACT>
 __global__ __launch_bounds__(kThreads, 3) void decode_split_mfma(DecodeParams p) {
   constexpr int KS = D / 32;          // k-steps of the score MFMA (32 features each)
   constexpr int DT = D / 16;          // 16-feature output tiles
@@ -379,7 +394,9 @@ __global__ __launch_bounds__(kThreads, 3) void decode_split_mfma(DecodeParams p)
   __shared__ float mrg_l[kWaves][16];
   float (*mrg_o)[G][D] = reinterpret_cast<float (*)[G][D]>(&vbuf[0][0]);
 
-  const int split = blockIdx.x, hk = blockIdx.y, b = blockIdx.z;
+  const int split = blockIdx.x, b = blockIdx.z;
+  const GroupMap<G, EXACT> gm(p, blockIdx.y);
+  const int hk = gm.hk;
   int n = p.Skv;
   if (p.kv_lens) n = min(max(p.kv_lens[b], 0), p.Skv);
   const int c0 = split * p.chunk;
@@ -387,17 +404,17 @@ __global__ __launch_bounds__(kThreads, 3) void decode_split_mfma(DecodeParams p)
   const int c1 = min(c0 + p.chunk, n);
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int qcol = lane & 15;          // query column (valid if < G)
+  const int qcol = lane & 15;          // query column (valid if < gm.g)
   const int grp = lane >> 4;           // 16-lane group
 
-  // Q^T as B operand: lane (qcol, grp) holds Q[h0 + qcol][32*ks + 8*grp .. +7].
+  // Q^T as B operand: lane (qcol, grp) holds Q[q0 + qcol][32*ks + 8*grp .. +7].
   bf16x8 qreg[KS];
   {
-    const uint16_t* qp = static_cast<const uint16_t*>(p.q) + ((int64_t)b * p.Hq + (int64_t)hk * G) * D;
+    const uint16_t* qp = static_cast<const uint16_t*>(p.q) + ((int64_t)b * p.Hq + gm.q0) * D;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       u32x4 w = {0u, 0u, 0u, 0u};
-      if (qcol < G) w = ld16(qp + (int64_t)qcol * D + 32 * ks + 8 * grp);
+      if (qcol < gm.g) w = ld16(qp + (int64_t)qcol * D + 32 * ks + 8 * grp);
       qreg[ks] = as_bf16x8(w);
     }
   }
@@ -516,7 +533,7 @@ __global__ __launch_bounds__(kThreads, 3) void decode_split_mfma(DecodeParams p)
     mrg_l[wave][qcol] = lsum;
   }
   __syncthreads();   // every wave is done with its V buffer before it is reused
-  if (qcol < G) {
+  if (qcol < gm.g) {
 #pragma unroll
     for (int t = 0; t < DT; ++t)
 #pragma unroll
@@ -524,7 +541,7 @@ __global__ __launch_bounds__(kThreads, 3) void decode_split_mfma(DecodeParams p)
   }
   __syncthreads();
   // merge the waves: thread tid handles (query, feature) pairs
-  for (int idx = tid; idx < G * D; idx += kThreads) {
+  for (int idx = tid; idx < gm.g * D; idx += kThreads) {
     const int qi = idx / D, d = idx % D;
     float M = kNegInf;
 #pragma unroll
@@ -536,7 +553,7 @@ __global__ __launch_bounds__(kThreads, 3) void decode_split_mfma(DecodeParams p)
       L += wt * mrg_l[w][qi];
       acc += wt * mrg_o[w][qi][d];
     }
-    const int64_t prow = ((int64_t)b * p.Hq + (int64_t)hk * G + qi) * p.n_split + split;
+    const int64_t prow = ((int64_t)b * p.Hq + gm.q0 + qi) * p.n_split + split;
     p.part_o[prow * D + d] = acc / L;
     if (d == 0) p.part_lse[prow] = M + log2_fast(L);
   }
@@ -564,9 +581,10 @@ __global__ __launch_bounds__(kThreads, 3) void decode_split_mfma(DecodeParams p)
 // distinct for every run and below B * H_kv + (number of workgroups).
 __device__ __forceinline__ int run_slot(int h, int u, int R) { return h + u / R; }
 
-// Exclusive prefix over batches of H_kv * ceil(n_b / kDecodeUnit) into pre[0..B]
-// (pre[B] = total units).  All threads of the workgroup take part.
-__device__ __forceinline__ void unit_prefix(const DecodeParams& p, int* pre, int* wave_tot) {
+// Exclusive prefix over batches of hv * ceil(n_b / kDecodeUnit) into pre[0..B]
+// (pre[B] = total units; hv: the virtual KV heads).  All threads of the
+// workgroup take part.
+__device__ __forceinline__ void unit_prefix(const DecodeParams& p, int hv, int* pre, int* wave_tot) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int per = (p.B + kThreads - 1) / kThreads;      // batches per thread (<= 8)
   const int b0 = tid * per;
@@ -578,7 +596,7 @@ __device__ __forceinline__ void unit_prefix(const DecodeParams& p, int* pre, int
     if (i < per && b0 + i < p.B) {
       int n = p.Skv;
       if (p.kv_lens) n = min(max(p.kv_lens[b0 + i], 0), p.Skv);
-      u = p.Hkv * ((n + kDecodeUnit - 1) / kDecodeUnit);
+      u = hv * ((n + kDecodeUnit - 1) / kDecodeUnit);
     }
     vals[i] = u;
     sum += u;
@@ -604,7 +622,7 @@ __device__ __forceinline__ void unit_prefix(const DecodeParams& p, int* pre, int
   __syncthreads();
 }
 
-template <int D, int G>
+template <int D, int G, bool EXACT>
 __global__ __launch_bounds__(kThreads, kDecodeWgPerCu) void decode_split_balanced(DecodeParams p) {
   constexpr int KS = D / 32;          // k-steps of the score MFMA (32 features each)
   constexpr int DT = D / 16;          // 16-feature output tiles
@@ -621,7 +639,9 @@ __global__ __launch_bounds__(kThreads, kDecodeWgPerCu) void decode_split_balance
   extern __shared__ int pre[];         // [B + 1], dynamic
   float (*mrg_o)[G][D] = reinterpret_cast<float (*)[G][D]>(&vbuf[0][0]);
 
-  unit_prefix(p, pre, wave_tot);
+  const int HV = EXACT ? p.Hkv : p.Hv;     // (virtual) KV heads: the units' head dimension
+  const int CB = EXACT ? G : p.cb;        // partial slots per run
+  unit_prefix(p, HV, pre, wave_tot);
   // Work coordinates are kept wave-uniform (scalar registers), so length and
   // page-table reads are scalar loads that never wait on the copies in flight.
   const int U = __builtin_amdgcn_readfirstlane(pre[p.B]);
@@ -672,11 +692,12 @@ __global__ __launch_bounds__(kThreads, kDecodeWgPerCu) void decode_split_balance
   }
   int b = lo;
   int pre_b = __builtin_amdgcn_readfirstlane(pre[b]);
-  int units_b = (__builtin_amdgcn_readfirstlane(pre[b + 1]) - pre_b) / p.Hkv;
-  int hk = (u - pre_b) / units_b;
+  int units_b = (__builtin_amdgcn_readfirstlane(pre[b + 1]) - pre_b) / HV;
+  int hk = (u - pre_b) / units_b;         // virtual KV head
   int k = (u - pre_b) % units_b;
 
   while (u < uend) {
+    const GroupMap<G, EXACT> gm(p, hk);
     int n = p.Skv;
     if (p.kv_lens) n = min(max(ld_const(p.kv_lens + b), 0), p.Skv);
     const int seg_start = u;
@@ -685,12 +706,12 @@ __global__ __launch_bounds__(kThreads, kDecodeWgPerCu) void decode_split_balance
     // Q^T as B operand: lane (qcol, grp) holds Q[h0 + qcol][32*ks + 8*grp .. +7].
     bf16x8 qreg[KS];
     {
-      const uint16_t* qp = static_cast<const uint16_t*>(p.q) + ((int64_t)b * p.Hq + (int64_t)hk * G) * D;
+      const uint16_t* qp = static_cast<const uint16_t*>(p.q) + ((int64_t)b * p.Hq + gm.q0) * D;
       u32x4 w[KS];
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         w[ks] = u32x4{0u, 0u, 0u, 0u};
-        if (qcol < G) w[ks] = ld16(qp + (int64_t)qcol * D + 32 * ks + 8 * grp);
+        if (qcol < gm.g) w[ks] = ld16(qp + (int64_t)qcol * D + 32 * ks + 8 * grp);
       }
       // Use the values here, so the wait for the Q loads is placed now and
       // not before every score MFMA of the step loop.
@@ -716,7 +737,7 @@ __global__ __launch_bounds__(kThreads, kDecodeWgPerCu) void decode_split_balance
     // operand layout would touch 16 rows per instruction.  Rows past the
     // length repeat row n-1.
     auto issue = [&](unsigned char* dst, const void* t, int base) __attribute__((always_inline)) {
-      const char* src = reinterpret_cast<const char*>(kv_row<D>(t, p, b, hk, base));
+      const char* src = reinterpret_cast<const char*>(kv_row<D>(t, p, b, gm.hk, base));
       if (base + 32 <= n) {
 #pragma unroll
         for (int w = 0; w < VP; ++w)
@@ -810,14 +831,14 @@ __global__ __launch_bounds__(kThreads, kDecodeWgPerCu) void decode_split_balance
       mrg_l[wave][qcol] = lsum;
     }
     __syncthreads();   // every wave is done with its V buffer before it is reused
-    if (qcol < G) {
+    if (qcol < gm.g) {
 #pragma unroll
       for (int t = 0; t < DT; ++t)
 #pragma unroll
         for (int i = 0; i < 4; ++i) mrg_o[wave][qcol][16 * t + 4 * grp + i] = oacc[t][i];
     }
     __syncthreads();
-    for (int idx = tid; idx < G * D; idx += kThreads) {
+    for (int idx = tid; idx < gm.g * D; idx += kThreads) {
       const int qi = idx / D, d = idx % D;
       float M = kNegInf;
 #pragma unroll
@@ -829,7 +850,7 @@ __global__ __launch_bounds__(kThreads, kDecodeWgPerCu) void decode_split_balance
         L += wt * mrg_l[w][qi];
         acc += wt * mrg_o[w][qi][d];
       }
-      const int64_t slot = (int64_t)run_slot(b * p.Hkv + hk, seg_start, R) * G + qi;
+      const int64_t slot = (int64_t)run_slot(b * HV + hk, seg_start, R) * CB + qi;
       p.part_o[slot * D + d] = acc / L;
       if (d == 0) p.part_lse[slot] = M + log2_fast(L);
     }
@@ -837,24 +858,34 @@ __global__ __launch_bounds__(kThreads, kDecodeWgPerCu) void decode_split_balance
 
     // next head: skip batches without units
     k = 0;
-    if (++hk == p.Hkv) {
+    if (++hk == HV) {
       hk = 0;
       do { ++b; } while (b < p.B && __builtin_amdgcn_readfirstlane(pre[b + 1]) == __builtin_amdgcn_readfirstlane(pre[b]));
       if (b < p.B) {
         pre_b = __builtin_amdgcn_readfirstlane(pre[b]);
-        units_b = (__builtin_amdgcn_readfirstlane(pre[b + 1]) - pre_b) / p.Hkv;
+        units_b = (__builtin_amdgcn_readfirstlane(pre[b + 1]) - pre_b) / HV;
       }
     }
   }
 }
 
-// Combine for the balanced pass: head (b, g) owns units [hs, he); its
-// segments start at hs and at every multiple of R inside (hs, he).
-template <int D, int G>
+// Combine for the balanced pass: (virtual) head (b, g) owns units [hs, he);
+// its segments start at hs and at every multiple of R inside (hs, he).
+template <int D, int G, bool EXACT>
 __global__ __launch_bounds__(64) void decode_combine_balanced(DecodeParams p) {
   const int hq = blockIdx.x, b = blockIdx.y;
   const int lane = threadIdx.x;
-  const int g = hq / G, qi = hq % G;
+  const int HV = EXACT ? p.Hkv : p.Hv;
+  const int CB = EXACT ? G : p.cb;
+  int g, qi;                            // virtual KV head, column within its block
+  if constexpr (EXACT) {
+    g = hq / G;
+    qi = hq % G;
+  } else {
+    const int grp = p.Hq / p.Hkv, hkr = hq / grp, j = hq - hkr * grp;
+    g = hkr * p.kv_div + j / p.cb;
+    qi = j % p.cb;
+  }
   // units before batch b, and in total (lane-strided sums over batches)
   int before = 0, total = 0, units_b = 0;
   for (int bb = lane; bb < p.B; bb += 64) {
@@ -871,21 +902,21 @@ __global__ __launch_bounds__(64) void decode_combine_balanced(DecodeParams p) {
     total += __shfl_xor(total, o, 64);
     units_b += __shfl_xor(units_b, o, 64);
   }
-  const int U = total * p.Hkv;
+  const int U = total * HV;
   const int R = (U + p.n_wg - 1) / p.n_wg;
-  const int hs = before * p.Hkv + g * units_b, he = hs + units_b;
+  const int hs = before * HV + g * units_b, he = hs + units_b;
   uint16_t* orow = static_cast<uint16_t*>(p.o) + ((int64_t)b * p.Hq + hq) * D;
   constexpr int PER = D / 64;
   float acc[PER];
 #pragma unroll
   for (int e = 0; e < PER; ++e) acc[e] = 0.f;
   float M = kNegInf;
-  const int head = b * p.Hkv + g;
+  const int head = b * HV + g;
   for (int s = hs; s < he; s = (s / R + 1) * R)
-    M = fmaxf(M, p.part_lse[(int64_t)run_slot(head, s, R) * G + qi]);
+    M = fmaxf(M, p.part_lse[(int64_t)run_slot(head, s, R) * CB + qi]);
   float Wsum = 0.f;
   for (int s = hs; s < he; s = (s / R + 1) * R) {
-    const int64_t slot = (int64_t)run_slot(head, s, R) * G + qi;
+    const int64_t slot = (int64_t)run_slot(head, s, R) * CB + qi;
     const float wt = exp2_fast(p.part_lse[slot] - M);
     Wsum += wt;
 #pragma unroll
@@ -932,48 +963,50 @@ __global__ __launch_bounds__(64) void decode_combine(DecodeParams p) {
   }
 }
 
-template <int D, int G>
+template <int D, int G, bool EXACT>
 hipError_t launch_balanced(const DecodeParams& p, hipStream_t stream) {
-  hipLaunchKernelGGL((decode_split_balanced<D, G>), dim3(p.n_wg), dim3(kThreads), (p.B + 1) * sizeof(int),
+  hipLaunchKernelGGL((decode_split_balanced<D, G, EXACT>), dim3(p.n_wg), dim3(kThreads), (p.B + 1) * sizeof(int),
                      stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((decode_combine_balanced<D, G>), dim3(p.Hq, p.B), dim3(64), 0, stream, p);
+  hipLaunchKernelGGL((decode_combine_balanced<D, G, EXACT>), dim3(p.Hq, p.B), dim3(64), 0, stream, p);
+  return hipGetLastError();
+}
+
+template <int D, int G, bool EXACT>
+hipError_t launch_group(const DecodeParams& p, hipStream_t stream) {
+  if (p.n_wg > 0) return launch_balanced<D, G, EXACT>(p, stream);
+  hipLaunchKernelGGL((decode_split_mfma<D, G, EXACT>), dim3(p.n_split, p.Hv, p.B), dim3(kThreads), 0, stream, p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((decode_combine<D>), dim3(p.Hq, p.B), dim3(64), 0, stream, p);
   return hipGetLastError();
 }
 
 template <int D>
 hipError_t launch_d(const DecodeParams& p, hipStream_t stream) {
   const int G = p.Hq / p.Hkv;
-  if (p.n_wg > 0) {
+  if (G == 1) {
+    hipLaunchKernelGGL((decode_split_valu<D>), dim3(p.n_split, p.Hkv, p.B), dim3(kThreads), 0, stream, p);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || p.n_split == 1) return e;   // one split: the split pass wrote O
+    hipLaunchKernelGGL((decode_combine<D>), dim3(p.Hq, p.B), dim3(64), 0, stream, p);
+    return hipGetLastError();
+  }
+  if (p.kv_div == 1 && p.cb == G) {
     switch (G) {
-      case 2: return launch_balanced<D, 2>(p, stream);
-      case 4: return launch_balanced<D, 4>(p, stream);
-      case 8: return launch_balanced<D, 8>(p, stream);
-      case 16: return launch_balanced<D, 16>(p, stream);
-      default: return hipErrorInvalidValue;
+      case 2: return launch_group<D, 2, true>(p, stream);
+      case 4: return launch_group<D, 4, true>(p, stream);
+      case 8: return launch_group<D, 8, true>(p, stream);
+      case 16: return launch_group<D, 16, true>(p, stream);
+      default: break;
     }
   }
-  // Matrix cores for groups of 2, 4, 8, 16 (grid over KV heads); the
-  // vector-ALU kernel for every other group size (grid over query heads).
-  const bool mfma = G == 2 || G == 4 || G == 8 || G == 16;
-  const dim3 grid(p.n_split, mfma ? p.Hkv : p.Hq, p.B);
-  switch (mfma ? G : 1) {
-    case 1:
-      if (G == 1) hipLaunchKernelGGL((decode_split_valu<D, true>), grid, dim3(kThreads), 0, stream, p);
-      else hipLaunchKernelGGL((decode_split_valu<D, false>), grid, dim3(kThreads), 0, stream, p);
-      break;
-    case 2: hipLaunchKernelGGL((decode_split_mfma<D, 2>), grid, dim3(kThreads), 0, stream, p); break;
-    case 4: hipLaunchKernelGGL((decode_split_mfma<D, 4>), grid, dim3(kThreads), 0, stream, p); break;
-    case 8: hipLaunchKernelGGL((decode_split_mfma<D, 8>), grid, dim3(kThreads), 0, stream, p); break;
-    case 16: hipLaunchKernelGGL((decode_split_mfma<D, 16>), grid, dim3(kThreads), 0, stream, p); break;
-    default: return hipErrorInvalidValue;
-  }
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  if (!mfma && p.n_split == 1) return hipSuccess;   // the split pass wrote O
-  hipLaunchKernelGGL((decode_combine<D>), dim3(p.Hq, p.B), dim3(64), 0, stream, p);
-  return hipGetLastError();
+  // any other group: column blocks of cb <= 16 query heads, padded to 4, 8 or 16
+  if (p.cb <= 4) return launch_group<D, 4, false>(p, stream);
+  if (p.cb <= 8) return launch_group<D, 8, false>(p, stream);
+  if (p.cb <= 16) return launch_group<D, 16, false>(p, stream);
+  return hipErrorInvalidValue;
 }
 
 }  // namespace

@@ -46,7 +46,7 @@ struct DecodeParams {
   void* o;
   const int32_t* kv_lens;  // device int32[B] or nullptr
   // Chunked pass: [B, Hq, n_split, d] and [B, Hq, n_split]; balanced pass:
-  // [B * Hkv + n_wg, G, d] and [B * Hkv + n_wg, G] (one slot per run).
+  // [B * Hv + n_wg, cb, d] and [B * Hv + n_wg, cb] (one slot per run).
   float* part_o;           // fp32 partial outputs, normalised
   float* part_lse;         // fp32 base-2 log-sum-exps
   int B, Hq, Hkv, Skv, d;
@@ -60,6 +60,13 @@ struct DecodeParams {
   // page_size is a multiple of kDecodeUnit; Skv = max_blocks * page_size.
   const int32_t* block_table;
   int max_blocks, page_size, num_pages;
+  // Query groups on the matrix cores (G = Hq / Hkv >= 2) are cut into
+  // kv_div column blocks of at most 16 query heads: virtual KV head vh
+  // (Hv = Hkv * kv_div of them) reads KV head vh / kv_div and holds query
+  // heads (vh / kv_div) * G + (vh % kv_div) * cb .. of it, cb of them (the
+  // last block of a head may hold fewer).  Groups of 2, 4, 8, 16: kv_div = 1,
+  // cb = G, Hv = Hkv.
+  int Hv, kv_div, cb;
 };
 
 // Largest batch the balanced (G >= 2) decode pass handles: its workgroups

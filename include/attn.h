@@ -173,11 +173,11 @@ attn_status_t attn_prefill_varlen_fwd(const void* q, const void* k, const void* 
  *   every key).  Size limits otherwise as attn_prefill_fwd.
  *   d: 64 or 128 (else ATTN_ERR_UNSUPPORTED).  dtype: ATTN_BF16 or
  *   ATTN_F32, any group size H_q/H_kv; q, the caches and o all have that
- *   dtype.  bf16 computes scores and P V with fp32 accumulation; groups of
- *   2, 4, 8 or 16 query heads run on the matrix cores (P rounded to bf16
- *   before P V), every other group size on the vector ALU one query head at
- *   a time (each query head streams its KV head's rows; the repeats are
- *   mostly served by cache).  fp32 computes in fp32 throughout.
+ *   dtype.  bf16 computes scores and P V with fp32 accumulation; one query
+ *   head per KV head on the vector ALU, larger groups on the matrix cores
+ *   (P rounded to bf16 before P V) in blocks of at most 16 query heads, each
+ *   block reading its KV head's rows once.  fp32 computes in fp32
+ *   throughout.
  *   workspace: device memory of at least
  *   attn_decode_workspace_bytes(B, H_q, H_kv, S_kv, d) bytes, 16-byte
  *   aligned, for the per-split partial results (fp32).  Its contents need no
@@ -187,8 +187,8 @@ attn_status_t attn_prefill_varlen_fwd(const void* q, const void* k, const void* 
  * Two kernels on `stream`: a split pass in which each workgroup streams one
  * chunk of the cache once and writes a normalised partial output with its
  * log-sum-exp, then a combine pass that merges the partials of each head
- * (the vector-ALU and fp32 passes skip it when every head has a single
- * split).
+ * (the one-head-per-KV-head and fp32 passes skip it when every head has a
+ * single split).
  * This is the Flash-Decoding split of "GPU learning day 24: Operator Fusion",
  * FAQ Q4, merged with the rescaling identity of that page's section 3.4 loop.
  */

@@ -145,13 +145,17 @@ DECODE_CASES = [
     # one split per head (capacity <= 512): the split pass writes O itself
     (4, 2, 2, 500, 128, [500, 1, 0, 257]),
     (2, 3, 3, 512, 64, [512, 77]),
-    # group sizes the matrix-core kernels do not take: the vector-ALU pass per
-    # query head (3, 5, 7, one KV head for 32 query heads; split and unsplit)
+    # other group sizes (3, 5, 7, one KV head for 32 query heads; split and
+    # unsplit): column blocks of at most 16 query heads on the matrix cores
     (2, 6, 2, 900, 128, [900, 333]),
     (2, 20, 4, 1300, 128, None),
     (3, 7, 1, 700, 64, [700, 1, 256]),
     (2, 32, 1, 1500, 128, [1500, 1024]),
     (4, 6, 2, 500, 128, [500, 0, 1, 257]),
+    # groups above 16: blocks of 10 + 10, of 9 + 8, and four blocks of 16
+    (2, 40, 2, 800, 64, [800, 129]),
+    (2, 17, 1, 600, 128, [600, 300]),
+    (1, 64, 1, 1000, 128, None),
 ]
 
 
@@ -184,15 +188,17 @@ def test_decode_split_count_invariance(chunk, monkeypatch):
 
 
 @pytest.mark.parametrize("wgs", ["1", "3", "7", "64", "100000"])
-def test_decode_balanced_partition_invariance(wgs, monkeypatch):
+@pytest.mark.parametrize("Hq", [8, 6, 40], ids=["group4", "group3", "group20"])
+def test_decode_balanced_partition_invariance(wgs, Hq, monkeypatch):
     """Query groups: the balanced pass spreads 128-key units over a forced
     number of workgroups (one workgroup walking every head, a few, more than
     there are units); every partition merges to the oracle's result.  Lengths
     include 0 and unit boundaries, and batches with no work sit between
-    others."""
-    B, Hq, Hkv, S, d = 9, 8, 2, 1100, 128
+    others.  Groups of 4, and of 3 and 20 (column blocks of 3, and 10 + 10
+    over two virtual heads per KV head)."""
+    B, Hkv, S, d = 9, 2, 1100, 128
     lens = [1100, 0, 128, 129, 0, 255, 256, 1, 0]
-    say(f"decode balanced workgroups={wgs}")
+    say(f"decode balanced workgroups={wgs} Hq={Hq}")
     x = make(B, Hq, Hkv, 1, S, d, seed=15, k_mult=4.0)
     monkeypatch.setenv("ATTN_DECODE_WORKGROUPS", wgs)
     o = attn.decode(x["q"], x["k"], x["v"], kv_lens=lens_tensor(lens))
@@ -216,18 +222,19 @@ def test_decode_balanced_many_batches():
     assert_close(o, ref, torch.bfloat16, "B=300")
 
 
-def test_decode_chunked_fallback_for_large_batches():
+@pytest.mark.parametrize("Hq", [2, 3, 18], ids=["group2", "group3", "group18"])
+def test_decode_chunked_fallback_for_large_batches(Hq):
     """Past the balanced pass's batch limit query groups use the chunked
-    split pass."""
-    B, Hq, Hkv, S, d = 2100, 2, 1, 40, 64
+    split pass (groups of 2; of 3 and 18 in column blocks)."""
+    B, Hkv, S, d = 2100, 1, 40, 64
     g = np.random.default_rng(10)
     lens = [int(x) for x in g.integers(0, S + 1, B)]
-    say("decode query groups, B=2100 (chunked pass)")
+    say(f"decode query groups, B=2100 Hq={Hq} (chunked pass)")
     x = make(B, Hq, Hkv, 1, S, d, seed=17)
     o = attn.decode(x["q"], x["k"], x["v"], kv_lens=lens_tensor(lens))
     torch.cuda.synchronize()
     ref = oracle.decode(x["q"].cpu(), x["k"].cpu(), x["v"].cpu(), lens, 1.0 / np.sqrt(d))
-    assert_close(o, ref, torch.bfloat16, "B=2100")
+    assert_close(o, ref, torch.bfloat16, f"B=2100 Hq={Hq}")
 
 
 # ---------------------------------------------------------------------------
