@@ -33,7 +33,6 @@ attn_status_t check_common(const void* q, const void* k, const void* v, const vo
   if (causal != 0 && causal != 1) return ATTN_ERR_SHAPE;
   if (d != 64 && d != 128 && d != 256) return ATTN_ERR_UNSUPPORTED;
   if (dtype != ATTN_F32 && dtype != ATTN_BF16) return ATTN_ERR_UNSUPPORTED;
-  if (d == 256 && dtype != ATTN_BF16) return ATTN_ERR_UNSUPPORTED;   // d = 256: bf16 prefill only
   if (!std::isfinite(scale)) return ATTN_ERR_VALUE;
   const bool has_q = (int64_t)B * S_q > 0;
   const bool has_kv = (int64_t)B * S_kv > 0;
@@ -80,22 +79,25 @@ int64_t virtual_heads(int32_t H_q, int32_t H_kv) {
   return (int64_t)H_kv * blocks;
 }
 
-bool mfma_group(int32_t H_q, int32_t H_kv) { return H_q / H_kv >= 2; }
+// Query groups run on the matrix cores at d = 64 and 128; one query head
+// per KV head, and every group at d = 256, on the vector-ALU pass over query
+// heads.
+bool mfma_group(int32_t H_q, int32_t H_kv, int32_t d) { return H_q / H_kv >= 2 && d != 256; }
 
 // Decode work decomposition.  Matrix-core query groups with at most
 // kDecodeMaxBatch sequences use the balanced pass: fixed units of
 // kDecodeUnit keys spread evenly over a persistent grid.  Otherwise the cache
 // is split into equal chunks per (batch, head): KV head for the matrix-core
 // kernels, query head for the vector-ALU one.
-bool decode_balanced(int32_t B, int32_t H_q, int32_t H_kv) {
-  return mfma_group(H_q, H_kv) && B <= attn::kDecodeMaxBatch;
+bool decode_balanced(int32_t B, int32_t H_q, int32_t H_kv, int32_t d) {
+  return mfma_group(H_q, H_kv, d) && B <= attn::kDecodeMaxBatch;
 }
 
 // Keys per split (or per unit on the balanced pass).  Test-only override for
 // the chunked pass: ATTN_DECODE_CHUNK (a positive multiple of 256) forces the
 // chunk so split-count invariance can be tested.
-int decode_chunk(int32_t B, int32_t H_q, int32_t H_kv, int32_t S_kv) {
-  if (decode_balanced(B, H_q, H_kv)) return attn::kDecodeUnit;
+int decode_chunk(int32_t B, int32_t H_q, int32_t H_kv, int32_t S_kv, int32_t d) {
+  if (decode_balanced(B, H_q, H_kv, d)) return attn::kDecodeUnit;
   if (const char* env = std::getenv("ATTN_DECODE_CHUNK")) {
     const long c = std::strtol(env, nullptr, 10);
     if (c >= 256 && c % 256 == 0 && c <= (1 << 30)) return (int)c;
@@ -105,7 +107,7 @@ int decode_chunk(int32_t B, int32_t H_q, int32_t H_kv, int32_t S_kv) {
   // 512 keys: each split costs a partial (d+1 floats) per query.  (For B64
   // H32 L4096 one split per head would stream at 6.95 TB/s, two, as chosen,
   // at 6.86, four at 6.75.)
-  const int64_t heads = (int64_t)B * (mfma_group(H_q, H_kv) ? virtual_heads(H_q, H_kv) : H_q);
+  const int64_t heads = (int64_t)B * (mfma_group(H_q, H_kv, d) ? virtual_heads(H_q, H_kv) : H_q);
   int64_t splits = heads >= 4096 ? 1 : (4096 + heads - 1) / heads;
   const int64_t max_splits = (S_kv + 511) / 512;
   if (splits > max_splits) splits = max_splits;
@@ -138,10 +140,10 @@ size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 // Partial rows (one per split and query head, or per run and query head on
 // the balanced pass) a decode of this shape may write.
-size_t partial_rows(int32_t B, int32_t H_q, int32_t H_kv, int32_t S_kv) {
-  const int chunk = decode_chunk(B, H_q, H_kv, S_kv);
+size_t partial_rows(int32_t B, int32_t H_q, int32_t H_kv, int32_t S_kv, int32_t d) {
+  const int chunk = decode_chunk(B, H_q, H_kv, S_kv, d);
   const int64_t n_split = (S_kv + chunk - 1) / chunk;
-  if (decode_balanced(B, H_q, H_kv)) {
+  if (decode_balanced(B, H_q, H_kv, d)) {
     // a run per (virtual head, workgroup range) boundary: fewer than
     // B*Hv + n_wg, with n_wg at most kDecodeMaxWg and at most the number of
     // units; cb partial rows per run
@@ -156,18 +158,18 @@ size_t partial_rows(int32_t B, int32_t H_q, int32_t H_kv, int32_t S_kv) {
 }
 
 size_t workspace_bytes(int32_t B, int32_t H_q, int32_t H_kv, int32_t S_kv, int32_t d) {
-  if (B <= 0 || S_kv <= 0 || H_q < 1 || H_kv < 1 || H_q % H_kv != 0 || (d != 64 && d != 128))
+  if (B <= 0 || S_kv <= 0 || H_q < 1 || H_kv < 1 || H_q % H_kv != 0 || (d != 64 && d != 128 && d != 256))
     return 0;
-  const size_t rows = partial_rows(B, H_q, H_kv, S_kv);
+  const size_t rows = partial_rows(B, H_q, H_kv, S_kv, d);
   return round_up(rows * d * sizeof(float), 256) + round_up(rows * sizeof(float), 256);
 }
 
-// What the decode kernels implement: d 64 or 128, bf16 or fp32, any group
-// size.
+// What the decode kernels implement: d 64, 128 or 256, bf16 or fp32, any
+// group size.
 bool decode_supported(int32_t H_q, int32_t H_kv, int32_t d, attn_dtype_t dtype) {
   (void)H_q;
   (void)H_kv;
-  if (d != 64 && d != 128) return false;
+  if (d != 64 && d != 128 && d != 256) return false;
   return dtype == ATTN_F32 || dtype == ATTN_BF16;
 }
 
@@ -238,8 +240,8 @@ attn_status_t run_decode(const void* q, const void* k, const void* v, void* o, i
     p.B = B; p.Hq = H_q; p.Hkv = H_kv; p.Skv = S_kv; p.d = d;
     p.block_table = block_table; p.max_blocks = max_blocks; p.page_size = page_size;
     p.num_pages = num_pages;
-    const size_t rows = partial_rows(B, H_q, H_kv, S_kv);
-    int64_t splits = (S_kv + decode_chunk(B, H_q, H_q, S_kv) - 1) / decode_chunk(B, H_q, H_q, S_kv);
+    const size_t rows = partial_rows(B, H_q, H_kv, S_kv, d);
+    int64_t splits = (S_kv + decode_chunk(B, H_q, H_q, S_kv, d) - 1) / decode_chunk(B, H_q, H_q, S_kv, d);
     const int64_t fit = (int64_t)(rows / ((size_t)B * H_q));
     if (splits > fit) splits = fit;
     if (splits < 1) splits = 1;
@@ -260,12 +262,12 @@ attn_status_t run_decode(const void* q, const void* k, const void* v, void* o, i
   p.B = B; p.Hq = H_q; p.Hkv = H_kv; p.Skv = S_kv; p.d = d;
   p.block_table = block_table; p.max_blocks = max_blocks; p.page_size = page_size;
   p.num_pages = num_pages;
-  p.chunk = decode_chunk(B, H_q, H_kv, S_kv);
+  p.chunk = decode_chunk(B, H_q, H_kv, S_kv, d);
   p.n_split = (S_kv + p.chunk - 1) / p.chunk;
   p.n_wg = 0;
   group_blocks(H_q, H_kv, &p.kv_div, &p.cb);
   p.Hv = H_kv * p.kv_div;
-  if (decode_balanced(B, H_q, H_kv)) {
+  if (decode_balanced(B, H_q, H_kv, d)) {
     // Persistent grid: kDecodeWgPerCu workgroups per compute unit (the
     // resident capacity), never more than there are units.  The contiguous and the paged cache use the same
     // grid, so both partition the keys alike and give the same bits.
@@ -283,7 +285,7 @@ attn_status_t run_decode(const void* q, const void* k, const void* v, void* o, i
     if (wg > attn::kDecodeMaxWg) wg = attn::kDecodeMaxWg;
     p.n_wg = (int)wg;
   }
-  const size_t rows = partial_rows(B, H_q, H_kv, S_kv);
+  const size_t rows = partial_rows(B, H_q, H_kv, S_kv, d);
   p.part_o = static_cast<float*>(workspace);
   p.part_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) +
                                         round_up(rows * d * sizeof(float), 256));
@@ -329,6 +331,7 @@ attn_status_t attn_prefill_fwd(const void* q, const void* k, const void* v, void
   attn_status_t st = check_common(q, k, v, o, B, H_q, H_kv, S_q, S_kv, d, causal, scale, dtype);
   if (st != ATTN_OK) return st;
   if (causal && S_q > S_kv) return ATTN_ERR_SHAPE;
+  if (d == 256 && dtype != ATTN_BF16) return ATTN_ERR_UNSUPPORTED;   // d = 256: bf16 prefill only
   if (dtype == ATTN_F32 && !grid_yz_ok(B, H_q)) return ATTN_ERR_SHAPE;
   if ((int64_t)B * S_q == 0) return ATTN_OK;  // nothing to compute
   hipStream_t s = static_cast<hipStream_t>(stream);

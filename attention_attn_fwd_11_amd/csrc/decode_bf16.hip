@@ -10,9 +10,14 @@
 // rescaling identity of that page's section 3.4 loop.
 //
 // Kernels
-//   decode_split_valu<D>     one query head per KV head (no reuse of K/V
-//                            across queries: a streaming dot product, so the
-//                            vector ALU is the right unit).
+//   decode_split_valu<D, STREAM>  one workgroup per (chunk, query head,
+//                            batch): a streaming dot product on the vector
+//                            ALU.  With one query head per KV head (STREAM)
+//                            there is no reuse of K/V across queries, so this
+//                            is the right unit.  At d = 256 it also serves
+//                            query groups, each query head streaming its KV
+//                            head's rows (the matrix-core kernels are built
+//                            for d = 64 and 128).
 //   decode_split_balanced<D, G, EXACT>  G >= 2 query heads share each KV
 //                            head, at most 2048 sequences: the queries form a
 //                            small matrix and QK^T and PV run on
@@ -183,25 +188,31 @@ struct WaveMerge {
 };
 
 // ---------------------------------------------------------------------------
-// G = 1: vector-ALU split kernel.
+// Vector-ALU split kernel: one query head per workgroup.
 //
 // Lane layout: a key row is D/8 16-byte pieces; LPK = D/8 lanes cover one key
 // and a wave load instruction covers KPI = 64/LPK consecutive keys (1 KiB,
 // fully coalesced).  Per iteration a wave handles 8 instructions' worth of
 // keys (KB = 8*KPI).  The 8 partial dot products per lane are reduced across
 // the LPK lanes of a key with a halving exchange, which leaves every key's
-// full score in one lane (pair).
+// full score in DUP = LPK/8 lanes.
+//
+// STREAM: one query head per KV head; K and V are read with the nontemporal
+// hint, each byte once.  Otherwise (query groups at d = 256) query head h
+// reads KV head h / (H_q / H_kv) with ordinary loads, so the group's repeats
+// may hit in cache.
 // ---------------------------------------------------------------------------
-template <int D>
+template <int D, bool STREAM>
 __global__ __launch_bounds__(kThreads) void decode_split_valu(DecodeParams p) {
   constexpr int LPK = D / 8;          // lanes per key row
   constexpr int KPI = 64 / LPK;       // keys per load instruction
   constexpr int KB = 8 * KPI;         // keys per wave iteration
-  constexpr int DUP = LPK / 8;        // lanes holding each reduced score (1 or 2)
+  constexpr int DUP = LPK / 8;        // lanes holding each reduced score (1, 2 or 4)
 
   __shared__ WaveMerge<D> merge;
 
   const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int hk = STREAM ? h : h / (p.Hq / p.Hkv);   // its KV head
   int n = p.Skv;
   if (p.kv_lens) n = min(max(p.kv_lens[b], 0), p.Skv);
   const int c0 = split * p.chunk;
@@ -220,7 +231,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_valu(DecodeParams p) {
   const u32x4 qv = ld16(static_cast<const uint16_t*>(p.q) + ((int64_t)b * p.Hq + h) * D + 8 * dc);
 
   // Which of the 8 keys of this lane's group its reduced score belongs to.
-  const int my_u = (LPK == 16) ? ((lane >> 1) & 7) : (lane & 7);
+  const int my_u = (lane / DUP) & 7;
 
   float m = kNegInf, lsum = 0.f;
   float o[8];
@@ -228,18 +239,18 @@ __global__ __launch_bounds__(kThreads) void decode_split_valu(DecodeParams p) {
   for (int e = 0; e < 8; ++e) o[e] = 0.f;
 
   for (int base = c0 + wave * KB; base < c1; base += kWaves * KB) {
-    const uint16_t* kp = kv_row<D>(p.k, p, b, h, base);   // rows base .. base+KB-1
-    const uint16_t* vp = kv_row<D>(p.v, p, b, h, base);
+    const uint16_t* kp = kv_row<D>(p.k, p, b, hk, base);   // rows base .. base+KB-1
+    const uint16_t* vp = kv_row<D>(p.v, p, b, hk, base);
     u32x4 kr[8], vr[8];
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       const int key = min(base + u * KPI + kg, c1 - 1) - base;
-      kr[u] = ld16_stream(kp + key * D + 8 * dc);
+      kr[u] = STREAM ? ld16_stream(kp + key * D + 8 * dc) : ld16(kp + key * D + 8 * dc);
     }
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       const int key = min(base + u * KPI + kg, c1 - 1) - base;
-      vr[u] = ld16_stream(vp + key * D + 8 * dc);
+      vr[u] = STREAM ? ld16_stream(vp + key * D + 8 * dc) : ld16(vp + key * D + 8 * dc);
     }
     // partial dots over this lane's 8 features
     float part[8];
@@ -274,7 +285,8 @@ __global__ __launch_bounds__(kThreads) void decode_split_valu(DecodeParams p) {
       const float send = bc ? part[0] : part[1];
       const float keep = bc ? part[1] : part[0];
       part[0] = keep + shfl_xor(send, MC);
-      if (LPK == 16) part[0] += shfl_xor(part[0], 1);
+#pragma unroll
+      for (int msk = LPK / 16; msk >= 1; msk >>= 1) part[0] += shfl_xor(part[0], msk);
     }
     float s = part[0];
     const int my_key = base + my_u * KPI + kg;
@@ -294,7 +306,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_valu(DecodeParams p) {
     // o += sum_u p_u v_u over this lane's 8 keys
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
-      const int src = kg * LPK + ((LPK == 16) ? 2 * u : u);
+      const int src = kg * LPK + u * DUP;
       const float pu = shfl(pr, src);
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
@@ -956,7 +968,10 @@ __global__ __launch_bounds__(64) void decode_combine(DecodeParams p) {
     for (int e = 0; e < PER; ++e) acc[e] = fmaf(wt, p.part_o[(prow0 + s) * D + PER * lane + e], acc[e]);
   }
   const float inv = ns > 0 ? 1.f / W : 0.f;
-  if (PER == 2) {
+  if constexpr (PER == 4) {
+    *reinterpret_cast<u32x2*>(orow + 4 * lane) = u32x2{pack_bf16x2(acc[0] * inv, acc[1] * inv),
+                                                       pack_bf16x2(acc[2] * inv, acc[3] * inv)};
+  } else if constexpr (PER == 2) {
     reinterpret_cast<uint32_t*>(orow)[lane] = pack_bf16x2(acc[0] * inv, acc[PER - 1] * inv);
   } else {
     orow[lane] = f32_to_bf16_bits(acc[0] * inv);
@@ -986,13 +1001,17 @@ hipError_t launch_group(const DecodeParams& p, hipStream_t stream) {
 template <int D>
 hipError_t launch_d(const DecodeParams& p, hipStream_t stream) {
   const int G = p.Hq / p.Hkv;
-  if (G == 1) {
-    hipLaunchKernelGGL((decode_split_valu<D>), dim3(p.n_split, p.Hkv, p.B), dim3(kThreads), 0, stream, p);
+  if (G == 1 || D == 256) {
+    // the vector-ALU pass over query heads (one per KV head, or d = 256)
+    if (G == 1) hipLaunchKernelGGL((decode_split_valu<D, true>), dim3(p.n_split, p.Hq, p.B), dim3(kThreads), 0, stream, p);
+    else hipLaunchKernelGGL((decode_split_valu<D, false>), dim3(p.n_split, p.Hq, p.B), dim3(kThreads), 0, stream, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || p.n_split == 1) return e;   // one split: the split pass wrote O
     hipLaunchKernelGGL((decode_combine<D>), dim3(p.Hq, p.B), dim3(64), 0, stream, p);
     return hipGetLastError();
   }
+  if constexpr (D == 256) return hipErrorInvalidValue;   // not reached
+  else {
   if (p.kv_div == 1 && p.cb == G) {
     switch (G) {
       case 2: return launch_group<D, 2, true>(p, stream);
@@ -1007,11 +1026,13 @@ hipError_t launch_d(const DecodeParams& p, hipStream_t stream) {
   if (p.cb <= 8) return launch_group<D, 8, false>(p, stream);
   if (p.cb <= 16) return launch_group<D, 16, false>(p, stream);
   return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace
 
 hipError_t launch_decode_bf16(const DecodeParams& p, hipStream_t stream) {
+  if (p.d == 256) return launch_d<256>(p, stream);
   return p.d == 64 ? launch_d<64>(p, stream) : launch_d<128>(p, stream);
 }
 

@@ -201,6 +201,7 @@ hipError_t launch_d(const DecodeParams& p, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_decode_f32(const DecodeParams& p, hipStream_t stream) {
+  if (p.d == 256) return launch_d<256>(p, stream);
   return p.d == 64 ? launch_d<64>(p, stream) : launch_d<128>(p, stream);
 }
 

@@ -87,8 +87,8 @@ def test_prefill_empty_is_noop(lib):
 @pytest.mark.parametrize("kw,code", [
     (dict(q=NULL), 1), (dict(o=NULL), 1), (dict(k=NULL), 1),
     (dict(Sq=2), 2), (dict(Sq=0), 2), (dict(Hq=6, Hkv=4), 2), (dict(B=-3), 2),
-    (dict(dtype=attn.ATTN_F32, d=96), 3), (dict(dtype=attn.ATTN_F32, d=256), 3), (dict(dtype=9), 3),
-    (dict(d=32), 3), (dict(d=256), 3),
+    (dict(dtype=attn.ATTN_F32, d=96), 3), (dict(dtype=9), 3),
+    (dict(d=32), 3), (dict(d=512), 3),
     (dict(ws=NULL), 5), (dict(wsb=16), 5), (dict(ws=MIS), 4), (dict(k=MIS), 4),
     (dict(scale=-math.inf), 7), (dict(Skv=(1 << 23) + 1, d=128), 2),
     # batches and query heads are grid dimensions of at most 65535
@@ -108,8 +108,8 @@ def decode_noalloc(q=P, k=P, v=P, o=P, B=1, Hq=2, Hkv=2, Sq=1, Skv=8, d=64, caus
 @pytest.mark.parametrize("kw,code", [
     (dict(q=NULL), 1), (dict(o=NULL), 1), (dict(k=NULL), 1),
     (dict(Sq=2), 2), (dict(Hq=6, Hkv=4), 2), (dict(B=-3), 2),
-    (dict(dtype=attn.ATTN_F32, d=96), 3), (dict(dtype=attn.ATTN_F32, d=256), 3), (dict(dtype=9), 3),
-    (dict(d=32), 3), (dict(d=256), 3),
+    (dict(dtype=attn.ATTN_F32, d=96), 3), (dict(dtype=9), 3),
+    (dict(d=32), 3), (dict(d=512), 3),
     (dict(q=MIS), 4), (dict(scale=math.nan), 7),
     # partials beyond the static scratch: B*H_q chunked splits of (d + 1) floats
     (dict(B=2048, Hq=32, Hkv=32, Skv=4096, d=128), 5),
@@ -197,8 +197,8 @@ def decode_paged(q=P, kp=P, vp=P, o=P, B=2, Hq=4, Hkv=4, d=64, scale=0.125, tabl
     (dict(pages=0), 2), (dict(Hq=6, Hkv=4), 2), (dict(B=-1), 2),
     (dict(max_blocks=1 << 24, page=256), 2),                   # capacity beyond int32
     (dict(max_blocks=(1 << 16) + 1, page=128, d=128), 2),      # one head's rows beyond 2^31 bytes
-    (dict(dtype=attn.ATTN_F32, d=96), 3), (dict(dtype=attn.ATTN_F32, d=256), 3), (dict(dtype=9), 3),
-    (dict(d=96), 3), (dict(d=256), 3),
+    (dict(dtype=attn.ATTN_F32, d=96), 3), (dict(dtype=9), 3),
+    (dict(d=96), 3), (dict(d=512), 3),
     (dict(q=MIS), 4), (dict(kp=MIS), 4), (dict(table=ctypes.c_void_p(0x10002)), 4), (dict(ws=MIS), 4),
     (dict(ws=NULL), 5), (dict(wsb=16), 5),
     (dict(scale=math.nan), 7),
@@ -222,6 +222,15 @@ def test_workspace_bytes(lib):
     # grows with heads and capacity; covers at least one partial per query head
     assert ws(64, 32, 32, 8192, 128) >= a
     assert ws(2, 4, 1, 100, 64) >= 2 * 4 * (64 + 1) * 4
+
+
+def test_workspace_head_dim_256(lib):
+    """d = 256 decodes (every group on the vector-ALU pass over query heads):
+    a partial of 256 + 1 floats per split and query head."""
+    ws = attn.attn_decode_workspace_bytes
+    # B4 H_q16 H_kv8: 64 query heads -> 8 splits of 512 keys for 4096 keys
+    assert ws(4, 16, 8, 4096, 256) >= 4 * 16 * 8 * (256 + 1) * 4
+    assert ws(1, 32, 32, 4096, 96) == 0
 
 
 def test_workspace_other_group_sizes(lib, monkeypatch):

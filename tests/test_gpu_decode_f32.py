@@ -49,6 +49,7 @@ CASES = [
     (3, 6, 2, 900, 128, [900, 300, 17]),
     (4, 4, 1, 2500, 128, [2500, 2048, 1, 999]),
     (2, 16, 16, 4096, 64, None),
+    (2, 4, 2, 900, 256, [900, 300]),
 ]
 
 

@@ -27,6 +27,7 @@ CASES = [
     (3, 4, 2, 768, 64, 128, [768, 200, 1]),                # d = 64, groups of 2, a one-key cache
     (2, 12, 4, 1280, 128, 256, [1280, 511]),               # groups of 3: vector-ALU pass per query head
     (2, 32, 1, 640, 64, 128, [640, 129]),                  # one KV head for 32 query heads
+    (2, 4, 2, 768, 256, 256, [768, 100]),                  # d = 256
 ]
 
 

@@ -152,6 +152,10 @@ DECODE_CASES = [
     (3, 7, 1, 700, 64, [700, 1, 256]),
     (2, 32, 1, 1500, 128, [1500, 1024]),
     (4, 6, 2, 500, 128, [500, 0, 1, 257]),
+    # d = 256: every query head on the vector-ALU pass (split, unsplit, groups)
+    (3, 4, 4, 1100, 256, [1100, 1, 0]),
+    (2, 8, 4, 1300, 256, [1300, 200]),
+    (2, 6, 2, 500, 256, [500, 17]),
     # groups above 16: blocks of 10 + 10, of 9 + 8, and four blocks of 16
     (2, 40, 2, 800, 64, [800, 129]),
     (2, 17, 1, 600, 128, [600, 300]),
