@@ -331,7 +331,6 @@ attn_status_t attn_prefill_fwd(const void* q, const void* k, const void* v, void
   attn_status_t st = check_common(q, k, v, o, B, H_q, H_kv, S_q, S_kv, d, causal, scale, dtype);
   if (st != ATTN_OK) return st;
   if (causal && S_q > S_kv) return ATTN_ERR_SHAPE;
-  if (d == 256 && dtype != ATTN_BF16) return ATTN_ERR_UNSUPPORTED;   // d = 256: bf16 prefill only
   if (dtype == ATTN_F32 && !grid_yz_ok(B, H_q)) return ATTN_ERR_SHAPE;
   if ((int64_t)B * S_q == 0) return ATTN_OK;  // nothing to compute
   hipStream_t s = static_cast<hipStream_t>(stream);

@@ -65,7 +65,9 @@ __global__ __launch_bounds__(kF32Threads) void prefill_f32_kernel(PrefillParams 
   constexpr int GROUPS = kF32Threads / (ROWS * kF32Parts);   // key groups
   constexpr int GT = ROWS * kF32Parts;                // threads per key group
   constexpr int F = D / kF32Parts;                    // features per lane
-  constexpr int KB = ROWS == 64 ? 32 : 1024 / D;      // keys per LDS block
+  // keys per LDS block (8-row tiles: 4 KiB of K per block, and 8 keys at
+  // d = 256 so the merge area fits the blocks)
+  constexpr int KB = ROWS == 64 ? 32 : (D == 256 ? 8 : 1024 / D);
   // K and V blocks of every group; after the loop the same memory holds each
   // group's state per row for the merge: o[D], m, l and two floats of
   // padding, so every record starts 16-byte aligned.
@@ -245,6 +247,7 @@ hipError_t launch(const PrefillParams& p, hipStream_t stream) {
 
 hipError_t launch_prefill_f32(const PrefillParams& p, hipStream_t stream) {
   if (p.d == 64) return p.causal ? launch<64, true>(p, stream) : launch<64, false>(p, stream);
+  if (p.d == 256) return p.causal ? launch<256, true>(p, stream) : launch<256, false>(p, stream);
   return p.causal ? launch<128, true>(p, stream) : launch<128, false>(p, stream);
 }
 

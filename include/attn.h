@@ -76,7 +76,7 @@ typedef enum {
  *   One head's rows (S_q*d or S_kv*d elements) span at most 2^31 - 1 bytes,
  *   B*H_q <= 2^30 - 1, and with ATTN_F32 B <= 65535 and H_q <= 65535 (the
  *   grid dimensions the kernel indexes them by); else ATTN_ERR_SHAPE.
- *   d: 64 or 128, and 256 with ATTN_BF16 (else ATTN_ERR_UNSUPPORTED).
+ *   d: 64, 128 or 256 (else ATTN_ERR_UNSUPPORTED).
  *   causal: 0 or 1; causal with S_q > S_kv is rejected (ATTN_ERR_SHAPE).
  *   scale: finite; the usual value is 1/sqrt(d).
  *   kv_lens: see above.

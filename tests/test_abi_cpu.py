@@ -64,12 +64,13 @@ def decode(q=P, k=P, v=P, o=P, B=1, Hq=2, Hkv=2, Sq=1, Skv=8, d=64, causal=0, sc
     (dict(q=NULL), 1), (dict(k=NULL), 1), (dict(v=NULL), 1), (dict(o=NULL), 1),
     (dict(B=-1), 2), (dict(Sq=-1), 2), (dict(Skv=-2), 2), (dict(Hq=0), 2), (dict(Hkv=0), 2),
     (dict(Hq=6, Hkv=4), 2), (dict(causal=2), 2), (dict(Sq=9, Skv=8, causal=1), 2),
-    (dict(d=96), 3), (dict(d=256, dtype=attn.ATTN_F32), 3), (dict(d=512), 3), (dict(dtype=5), 3),
+    (dict(d=96), 3), (dict(d=512), 3), (dict(dtype=5), 3),
     (dict(q=MIS), 4), (dict(o=MIS), 4), (dict(k=MIS), 4), (dict(v=MIS), 4),
     (dict(scale=math.inf), 7), (dict(scale=math.nan), 7),
     # one head's rows must span at most 2^31 - 1 bytes
     (dict(Skv=(1 << 23) + 1, d=128), 2), (dict(Sq=(1 << 23) + 1, Skv=(1 << 23) + 1, causal=0, d=128), 2),
     (dict(Skv=(1 << 22) + 1, d=128, dtype=attn.ATTN_F32), 2),
+    (dict(Skv=(1 << 21) + 1, d=256, dtype=attn.ATTN_F32), 2),
     # B * H_q at most 2^30 - 1; fp32 indexes B and H_q by grid dimensions of at most 65535
     (dict(B=1 << 15, Hq=1 << 15, Hkv=1 << 15), 2),
     (dict(B=65536, Hq=1, Hkv=1, dtype=attn.ATTN_F32), 2), (dict(B=1, Hq=65536, Hkv=1, dtype=attn.ATTN_F32), 2),

@@ -84,6 +84,11 @@ PREFILL_CASES = [
     # fp32 grids of >= 512 64-row tiles take the 64-row, one-group shape
     (1, 64, 8, 520, 520, 64, True, None, "f32"),
     (1, 64, 16, 512, 600, 128, True, [600], "f32"),
+    # fp32 at d = 256: 8-row tiles with key groups (8-key blocks), and the
+    # 64-row shape
+    (2, 4, 2, 150, 300, 256, True, [300, 41], "f32"),
+    (1, 3, 3, 90, 90, 256, False, None, "f32"),
+    (1, 64, 64, 520, 520, 256, True, None, "f32"),
 ]
 
 
