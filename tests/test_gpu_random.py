@@ -1,0 +1,109 @@
+"""Seeded random sweep over the entry points' configuration space, each case
+compared over its whole output with the fp64 oracle at its dtype's bar.
+
+Every case is drawn from its own seed (the test id names it), so a failure
+names a reproducible configuration: prefill in bf16 and fp32 at d = 64, 128
+and 256, causal or not, query groups of any size, ragged key lengths with
+empty sequences and S_q < S_kv; decode in bf16 and fp32 over contiguous and
+paged caches, query groups from 1 to 40 (exact matrix-core groups, column
+blocks, one KV head for many query heads), ragged and empty lengths.
+Shapes stay small enough that the oracle takes well under a second.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import attention_attn_fwd_11_amd as attn
+import oracle
+from attention_attn_fwd_11_amd import workloads as wl
+from tests.gpu_util import assert_close
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    torch.cuda.init()
+    yield
+    torch.cuda.synchronize()
+
+
+def draw_lengths(g, B, S):
+    """Per-sequence key lengths in [0, S] with some empty, full and one-key
+    sequences (in a causal prefill, rows of a sequence shorter than S_q that
+    see no key give zeros)."""
+    lens = [int(x) for x in g.integers(0, S + 1, B)]
+    if B > 1:
+        lens[int(g.integers(0, B))] = S
+    if B > 2 and g.random() < 0.5:
+        lens[int(g.integers(0, B))] = 0
+    if B > 3 and g.random() < 0.5:
+        lens[int(g.integers(0, B))] = 1
+    return lens
+
+
+@pytest.mark.parametrize("seed", range(60))
+def test_random_prefill(seed):
+    g = np.random.default_rng(1000 + seed)
+    dtype = "f32" if g.random() < 0.3 else "bf16"
+    d = int(g.choice([64, 128, 256]))
+    Hkv = int(g.choice([1, 2, 3]))
+    G = int(g.choice([1, 1, 2, 3, 4, 5, 8]))
+    Hq = Hkv * G
+    B = int(g.integers(1, 4))
+    Skv = int(g.integers(1, 700))
+    causal = bool(g.random() < 0.7)
+    Sq = Skv if g.random() < 0.5 else int(g.integers(1, Skv + 1))
+    lens = draw_lengths(g, B, Skv) if g.random() < 0.5 else None
+    scale = float(g.choice([1.0 / np.sqrt(d), 0.5, -0.2]))
+    case = dict(dtype=dtype, d=d, B=B, Hq=Hq, Hkv=Hkv, Sq=Sq, Skv=Skv, causal=causal, lens=lens,
+                scale=scale)
+    say(f"random prefill {seed}: {case}")
+    x = wl.random_problem(B, Hq, Hkv, Sq, Skv, d, dtype=dtype, device=DEV, seed=seed)
+    lt = None if lens is None else torch.tensor(lens, dtype=torch.int32, device=DEV)
+    o = attn.prefill(x["q"], x["k"], x["v"], causal=causal, scale=scale, kv_lens=lt)
+    torch.cuda.synchronize()
+    ref = oracle.attention(x["q"].cpu(), x["k"].cpu(), x["v"].cpu(), causal, scale, kv_lens=lens)
+    assert_close(o, ref, x["q"].dtype, f"random prefill {seed} {case}")
+
+
+@pytest.mark.parametrize("seed", range(60))
+def test_random_decode(seed):
+    g = np.random.default_rng(2000 + seed)
+    dtype = "f32" if g.random() < 0.25 else "bf16"
+    d = int(g.choice([64, 128, 256]))
+    Hkv = int(g.choice([1, 2, 4]))
+    G = int(g.choice([1, 2, 3, 4, 6, 7, 8, 12, 16, 20, 40]))
+    Hq = Hkv * G
+    B = int(g.integers(1, 6))
+    S = int(g.integers(1, 1600))
+    paged = bool(g.random() < 0.35)
+    if paged:
+        S = max(S, 128)
+    lens = draw_lengths(g, B, S)
+    scale = float(g.choice([1.0 / np.sqrt(d), 0.3, -0.25]))
+    case = dict(dtype=dtype, d=d, B=B, Hq=Hq, Hkv=Hkv, S=S, paged=paged, lens=lens, scale=scale)
+    say(f"random decode {seed}: {case}")
+    x = wl.random_problem(B, Hq, Hkv, 1, S, d, dtype=dtype, device=DEV, seed=seed)
+    lt = torch.tensor(lens, dtype=torch.int32, device=DEV)
+    if paged:
+        P = int(g.choice([128, 256]))
+        kp, vp, table = wl.paged_cache(x["k"], x["v"], lens, P, seed=seed)
+        o = attn.decode_paged(x["q"], kp, vp, table, kv_lens=lt, scale=scale)
+    else:
+        o = attn.decode(x["q"], x["k"], x["v"], kv_lens=lt, scale=scale)
+    torch.cuda.synchronize()
+    ref = oracle.decode(x["q"].cpu(), x["k"].cpu(), x["v"].cpu(), lens, scale)
+    assert_close(o, ref, x["q"].dtype, f"random decode {seed} {case}")
+    assert torch.all(o[[b for b, n in enumerate(lens) if n == 0]] == 0)
