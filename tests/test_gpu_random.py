@@ -6,7 +6,8 @@ names a reproducible configuration: prefill in bf16 and fp32 at d = 64, 128
 and 256, causal or not, query groups of any size, ragged key lengths with
 empty sequences and S_q < S_kv; decode in bf16 and fp32 over contiguous and
 paged caches, query groups from 1 to 40 (exact matrix-core groups, column
-blocks, one KV head for many query heads), ragged and empty lengths.
+blocks, one KV head for many query heads), ragged and empty lengths; packed
+variable-length prefill over random query and key lengths.
 Shapes stay small enough that the oracle takes well under a second.
 """
 import sys
@@ -107,3 +108,44 @@ def test_random_decode(seed):
     ref = oracle.decode(x["q"].cpu(), x["k"].cpu(), x["v"].cpu(), lens, scale)
     assert_close(o, ref, x["q"].dtype, f"random decode {seed} {case}")
     assert torch.all(o[[b for b, n in enumerate(lens) if n == 0]] == 0)
+
+
+@pytest.mark.parametrize("seed", range(30))
+def test_random_varlen(seed):
+    """Packed sequences of random query and key lengths (some empty, some with
+    fewer keys than queries), any group size, d = 64, 128, 256, causal or
+    not, compared with the oracle sequence by sequence."""
+    g = np.random.default_rng(3000 + seed)
+    d = int(g.choice([64, 128, 256]))
+    Hkv = int(g.choice([1, 2, 4]))
+    Hq = Hkv * int(g.choice([1, 2, 3, 4, 8]))
+    nseq = int(g.integers(1, 9))
+    causal = bool(g.random() < 0.7)
+    q_lens = [int(n) for n in g.integers(0, 600, nseq)]
+    k_lens = [int(q + g.integers(0, 300)) if g.random() < 0.8 else int(g.integers(0, 600))
+              for q in q_lens]
+    if nseq > 2 and g.random() < 0.5:
+        q_lens[int(g.integers(0, nseq))] = 0
+    if max(q_lens) == 0:
+        q_lens[0] = 1
+    scale = float(g.choice([1.0 / np.sqrt(d), 0.4, -0.3]))
+    case = dict(d=d, Hq=Hq, Hkv=Hkv, causal=causal, q_lens=q_lens, k_lens=k_lens, scale=scale)
+    say(f"random varlen {seed}: {case}")
+    x = wl.varlen_problem(q_lens, k_lens, Hq, Hkv, d, device=DEV, seed=seed)
+    o = attn.prefill_varlen(x["q"], x["k"], x["v"], x["cu_q"], x["cu_k"], max(q_lens), max(max(k_lens), 1),
+                            causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    cq, ck = x["cu_q"].tolist(), x["cu_k"].tolist()
+    q, k, v, oc = x["q"].cpu(), x["k"].cpu(), x["v"].cpu(), o.cpu()
+    for b, (s, n) in enumerate(zip(q_lens, k_lens)):
+        if s == 0:
+            continue
+        got = oc[cq[b]:cq[b + 1]].permute(1, 0, 2).unsqueeze(0)
+        if n == 0:
+            assert torch.count_nonzero(got) == 0, f"seed {seed} sequence {b} has no key: O must be 0"
+            continue
+        qb = q[cq[b]:cq[b + 1]].permute(1, 0, 2).unsqueeze(0).contiguous()
+        kb = k[ck[b]:ck[b + 1]].permute(1, 0, 2).unsqueeze(0).contiguous()
+        vb = v[ck[b]:ck[b + 1]].permute(1, 0, 2).unsqueeze(0).contiguous()
+        ref = oracle.attention(qb, kb, vb, causal, scale)
+        assert_close(got, ref, torch.bfloat16, f"random varlen {seed} {case} sequence {b}")
