@@ -7,7 +7,8 @@ and 256, causal or not, query groups of any size, ragged key lengths with
 empty sequences and S_q < S_kv; decode in bf16 and fp32 over contiguous and
 paged caches, query groups from 1 to 40 (exact matrix-core groups, column
 blocks, one KV head for many query heads), ragged and empty lengths; packed
-variable-length prefill over random query and key lengths.
+variable-length prefill over random query and key lengths; the rotary
+prefill in both K placements.
 Shapes stay small enough that the oracle takes well under a second.
 """
 import sys
@@ -149,3 +150,43 @@ def test_random_varlen(seed):
         vb = v[ck[b]:ck[b + 1]].permute(1, 0, 2).unsqueeze(0).contiguous()
         ref = oracle.attention(qb, kb, vb, causal, scale)
         assert_close(got, ref, torch.bfloat16, f"random varlen {seed} {case} sequence {b}")
+
+
+@pytest.mark.parametrize("seed", range(20))
+def test_random_rope_prefill(seed):
+    """Prefill with the rotary embedding, K rotated in the kernel and by the
+    pre-pass (the same bits), against the oracle that rotates Q and K first.
+
+    The scale is +-1/sqrt(d): the kernels round the rotated Q and K to bf16
+    (the MFMA operands) where the oracle keeps the fp64 rotation, and a larger
+    |scale| sharpens the softmax until that rounding alone leaves the bf16
+    bar (seed 4 at scale -0.2: 2.7e-2 max-abs, the same as the oracle fed
+    with bf16-rounded rotations, computed on the CPU)."""
+    from oracle import rope as orope
+    g = np.random.default_rng(4000 + seed)
+    d = int(g.choice([64, 128, 256]))
+    Hkv = int(g.choice([1, 2]))
+    Hq = Hkv * int(g.choice([1, 2, 3, 4]))
+    B = int(g.integers(1, 4))
+    Skv = int(g.integers(1, 600))
+    causal = bool(g.random() < 0.7)
+    Sq = Skv if g.random() < 0.5 else int(g.integers(1, Skv + 1))
+    lens = draw_lengths(g, B, Skv) if g.random() < 0.5 else None
+    spare = int(g.integers(0, 20))
+    scale = float(g.choice([1.0, -1.0])) / np.sqrt(d)
+    case = dict(d=d, B=B, Hq=Hq, Hkv=Hkv, Sq=Sq, Skv=Skv, causal=causal, lens=lens, spare=spare,
+                scale=scale)
+    say(f"random rope prefill {seed}: {case}")
+    x = wl.random_problem(B, Hq, Hkv, Sq, Skv, d, dtype="bf16", device=DEV, seed=seed)
+    table = wl.rope_table(Skv + spare, d, device=DEV)
+    lt = None if lens is None else torch.tensor(lens, dtype=torch.int32, device=DEV)
+    ws = torch.empty(max(attn.attn_prefill_rope_workspace_bytes(B, Hkv, Skv, d), 16), dtype=torch.uint8,
+                     device=DEV)
+    o = attn.prefill(x["q"], x["k"], x["v"], causal=causal, scale=scale, kv_lens=lt, rope=table)
+    o2 = attn.prefill(x["q"], x["k"], x["v"], causal=causal, scale=scale, kv_lens=lt, rope=table,
+                      rope_workspace=ws)
+    torch.cuda.synchronize()
+    ref = orope.attention_rope(x["q"].cpu(), x["k"].cpu(), x["v"].cpu(), causal, scale, table.cpu(),
+                               kv_lens=lens)
+    assert_close(o, ref, torch.bfloat16, f"random rope {seed} {case}")
+    assert torch.equal(o, o2), f"random rope {seed}: the two K placements differ"
