@@ -79,10 +79,12 @@ int64_t virtual_heads(int32_t H_q, int32_t H_kv) {
   return (int64_t)H_kv * blocks;
 }
 
-// Query groups run on the matrix cores at d = 64 and 128; one query head
-// per KV head, and every group at d = 256, on the vector-ALU pass over query
-// heads.
-bool mfma_group(int32_t H_q, int32_t H_kv, int32_t d) { return H_q / H_kv >= 2 && d != 256; }
+// Query groups run on the matrix cores; one query head per KV head on the
+// vector-ALU pass.
+bool mfma_group(int32_t H_q, int32_t H_kv, int32_t d) {
+  (void)d;
+  return H_q / H_kv >= 2;
+}
 
 // Decode work decomposition.  Matrix-core query groups with at most
 // kDecodeMaxBatch sequences use the balanced pass: fixed units of
@@ -90,7 +92,8 @@ bool mfma_group(int32_t H_q, int32_t H_kv, int32_t d) { return H_q / H_kv >= 2 &
 // is split into equal chunks per (batch, head): KV head for the matrix-core
 // kernels, query head for the vector-ALU one.
 bool decode_balanced(int32_t B, int32_t H_q, int32_t H_kv, int32_t d) {
-  return mfma_group(H_q, H_kv, d) && B <= attn::kDecodeMaxBatch;
+  // built for d = 64 and 128; d = 256 groups take the chunked pass
+  return mfma_group(H_q, H_kv, d) && d != 256 && B <= attn::kDecodeMaxBatch;
 }
 
 // Keys per split (or per unit on the balanced pass).  Test-only override for

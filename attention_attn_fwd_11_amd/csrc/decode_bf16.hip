@@ -10,16 +10,12 @@
 // rescaling identity of that page's section 3.4 loop.
 //
 // Kernels
-//   decode_split_valu<D, STREAM>  one workgroup per (chunk, query head,
-//                            batch): a streaming dot product on the vector
-//                            ALU.  With one query head per KV head (STREAM)
-//                            there is no reuse of K/V across queries, so this
-//                            is the right unit.  At d = 256 it also serves
-//                            query groups, each query head streaming its KV
-//                            head's rows (the matrix-core kernels are built
-//                            for d = 64 and 128).
+//   decode_split_valu<D>     one query head per KV head (no reuse of K/V
+//                            across queries: a streaming dot product, so the
+//                            vector ALU is the right unit).
 //   decode_split_balanced<D, G, EXACT>  G >= 2 query heads share each KV
-//                            head, at most 2048 sequences: the queries form a
+//                            head, d = 64 or 128, at most 2048 sequences: the
+//                            queries form a
 //                            small matrix and QK^T and PV run on
 //                            v_mfma_f32_16x16x32_bf16 with the group padded to
 //                            16 columns; a persistent pass over equal units of
@@ -28,7 +24,7 @@
 //                            computes.  decode_combine_balanced merges.
 //   decode_split_mfma<D, G, EXACT>  the same contraction on a grid of
 //                            (chunk, KV head, batch) workgroups, for larger
-//                            batches.
+//                            batches and for d = 256.
 //   EXACT: groups of exactly G = 2, 4, 8 or 16 query heads.  Otherwise any
 //   group size: each KV head's group is cut into column blocks of at most 16
 //   query heads (virtual KV heads, see GroupMap), each reading the KV head
@@ -188,7 +184,7 @@ struct WaveMerge {
 };
 
 // ---------------------------------------------------------------------------
-// Vector-ALU split kernel: one query head per workgroup.
+// G = 1: vector-ALU split kernel.
 //
 // Lane layout: a key row is D/8 16-byte pieces; LPK = D/8 lanes cover one key
 // and a wave load instruction covers KPI = 64/LPK consecutive keys (1 KiB,
@@ -197,12 +193,8 @@ struct WaveMerge {
 // the LPK lanes of a key with a halving exchange, which leaves every key's
 // full score in DUP = LPK/8 lanes.
 //
-// STREAM: one query head per KV head; K and V are read with the nontemporal
-// hint, each byte once.  Otherwise (query groups at d = 256) query head h
-// reads KV head h / (H_q / H_kv) with ordinary loads, so the group's repeats
-// may hit in cache.
 // ---------------------------------------------------------------------------
-template <int D, bool STREAM>
+template <int D>
 __global__ __launch_bounds__(kThreads) void decode_split_valu(DecodeParams p) {
   constexpr int LPK = D / 8;          // lanes per key row
   constexpr int KPI = 64 / LPK;       // keys per load instruction
@@ -212,7 +204,6 @@ __global__ __launch_bounds__(kThreads) void decode_split_valu(DecodeParams p) {
   __shared__ WaveMerge<D> merge;
 
   const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
-  const int hk = STREAM ? h : h / (p.Hq / p.Hkv);   // its KV head
   int n = p.Skv;
   if (p.kv_lens) n = min(max(p.kv_lens[b], 0), p.Skv);
   const int c0 = split * p.chunk;
@@ -239,18 +230,18 @@ __global__ __launch_bounds__(kThreads) void decode_split_valu(DecodeParams p) {
   for (int e = 0; e < 8; ++e) o[e] = 0.f;
 
   for (int base = c0 + wave * KB; base < c1; base += kWaves * KB) {
-    const uint16_t* kp = kv_row<D>(p.k, p, b, hk, base);   // rows base .. base+KB-1
-    const uint16_t* vp = kv_row<D>(p.v, p, b, hk, base);
+    const uint16_t* kp = kv_row<D>(p.k, p, b, h, base);   // rows base .. base+KB-1
+    const uint16_t* vp = kv_row<D>(p.v, p, b, h, base);
     u32x4 kr[8], vr[8];
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       const int key = min(base + u * KPI + kg, c1 - 1) - base;
-      kr[u] = STREAM ? ld16_stream(kp + key * D + 8 * dc) : ld16(kp + key * D + 8 * dc);
+      kr[u] = ld16_stream(kp + key * D + 8 * dc);
     }
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       const int key = min(base + u * KPI + kg, c1 - 1) - base;
-      vr[u] = STREAM ? ld16_stream(vp + key * D + 8 * dc) : ld16(vp + key * D + 8 * dc);
+      vr[u] = ld16_stream(vp + key * D + 8 * dc);
     }
     // partial dots over this lane's 8 features
     float part[8];
@@ -391,8 +382,11 @@ struct GroupMap {
 // reads V^T with the LDS transpose read, so no workgroup barrier is needed
 // inside the loop.
 // ---------------------------------------------------------------------------
+// At d = 256 the fragments (K 64, V 64, O 64, Q 32 registers) and the rest
+// exceed 256 registers, so one wave per SIMD (a 64.5 KiB workgroup per CU,
+// 128 KiB of K and V in flight); d = 64 and 128 fit three.
 template <int D, int G, bool EXACT>
-__global__ __launch_bounds__(kThreads, 3) void decode_split_mfma(DecodeParams p) {
+__global__ __launch_bounds__(kThreads, (D == 256 ? 1 : 3)) void decode_split_mfma(DecodeParams p) {
   constexpr int KS = D / 32;          // k-steps of the score MFMA (32 features each)
   constexpr int DT = D / 16;          // 16-feature output tiles
   constexpr int SLOTS = D / 8;        // 16-byte slots per V row
@@ -990,7 +984,9 @@ hipError_t launch_balanced(const DecodeParams& p, hipStream_t stream) {
 
 template <int D, int G, bool EXACT>
 hipError_t launch_group(const DecodeParams& p, hipStream_t stream) {
-  if (p.n_wg > 0) return launch_balanced<D, G, EXACT>(p, stream);
+  if constexpr (D != 256) {   // the balanced pass is built for d = 64 and 128
+    if (p.n_wg > 0) return launch_balanced<D, G, EXACT>(p, stream);
+  }
   hipLaunchKernelGGL((decode_split_mfma<D, G, EXACT>), dim3(p.n_split, p.Hv, p.B), dim3(kThreads), 0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -1001,17 +997,14 @@ hipError_t launch_group(const DecodeParams& p, hipStream_t stream) {
 template <int D>
 hipError_t launch_d(const DecodeParams& p, hipStream_t stream) {
   const int G = p.Hq / p.Hkv;
-  if (G == 1 || D == 256) {
-    // the vector-ALU pass over query heads (one per KV head, or d = 256)
-    if (G == 1) hipLaunchKernelGGL((decode_split_valu<D, true>), dim3(p.n_split, p.Hq, p.B), dim3(kThreads), 0, stream, p);
-    else hipLaunchKernelGGL((decode_split_valu<D, false>), dim3(p.n_split, p.Hq, p.B), dim3(kThreads), 0, stream, p);
+  if (G == 1) {
+    hipLaunchKernelGGL((decode_split_valu<D>), dim3(p.n_split, p.Hq, p.B), dim3(kThreads), 0, stream, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || p.n_split == 1) return e;   // one split: the split pass wrote O
     hipLaunchKernelGGL((decode_combine<D>), dim3(p.Hq, p.B), dim3(64), 0, stream, p);
     return hipGetLastError();
   }
-  if constexpr (D == 256) return hipErrorInvalidValue;   // not reached
-  else {
+  {
   if (p.kv_div == 1 && p.cb == G) {
     switch (G) {
       case 2: return launch_group<D, 2, true>(p, stream);

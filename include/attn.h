@@ -174,11 +174,10 @@ attn_status_t attn_prefill_varlen_fwd(const void* q, const void* k, const void* 
  *   d: 64, 128 or 256 (else ATTN_ERR_UNSUPPORTED).  dtype: ATTN_BF16 or
  *   ATTN_F32, any group size H_q/H_kv; q, the caches and o all have that
  *   dtype.  bf16 computes scores and P V with fp32 accumulation; one query
- *   head per KV head on the vector ALU, larger groups at d = 64 and 128 on
- *   the matrix cores (P rounded to bf16 before P V) in blocks of at most 16
- *   query heads, each block reading its KV head's rows once; at d = 256
- *   every query head on the vector ALU (a group's query heads each read
- *   their KV head's rows).  fp32 computes in fp32 throughout.
+ *   head per KV head on the vector ALU, larger groups on the matrix cores
+ *   (P rounded to bf16 before P V) in blocks of at most 16 query heads, each
+ *   block reading its KV head's rows once.  fp32 computes in fp32
+ *   throughout.
  *   workspace: device memory of at least
  *   attn_decode_workspace_bytes(B, H_q, H_kv, S_kv, d) bytes, 16-byte
  *   aligned, for the per-split partial results (fp32).  Its contents need no
