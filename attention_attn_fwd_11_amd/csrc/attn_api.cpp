@@ -92,8 +92,7 @@ bool mfma_group(int32_t H_q, int32_t H_kv, int32_t d) {
 // is split into equal chunks per (batch, head): KV head for the matrix-core
 // kernels, query head for the vector-ALU one.
 bool decode_balanced(int32_t B, int32_t H_q, int32_t H_kv, int32_t d) {
-  // built for d = 64 and 128; d = 256 groups take the chunked pass
-  return mfma_group(H_q, H_kv, d) && d != 256 && B <= attn::kDecodeMaxBatch;
+  return mfma_group(H_q, H_kv, d) && B <= attn::kDecodeMaxBatch;
 }
 
 // Keys per split (or per unit on the balanced pass).  Test-only override for
@@ -271,14 +270,14 @@ attn_status_t run_decode(const void* q, const void* k, const void* v, void* o, i
   group_blocks(H_q, H_kv, &p.kv_div, &p.cb);
   p.Hv = H_kv * p.kv_div;
   if (decode_balanced(B, H_q, H_kv, d)) {
-    // Persistent grid: kDecodeWgPerCu workgroups per compute unit (the
-    // resident capacity), never more than there are units.  The contiguous and the paged cache use the same
+    // Persistent grid: the resident capacity (two workgroups per compute
+    // unit, one at d = 256), never more than there are units.  The contiguous and the paged cache use the same
     // grid, so both partition the keys alike and give the same bits.
     // Test-only override: ATTN_DECODE_WORKGROUPS.
     int dev = 0;
     const int cus = device_cus(&dev);
     if (cus <= 0) return hip_fail("hipDeviceGetAttribute(multiprocessor count)", hipGetLastError());
-    int64_t wg = (int64_t)attn::kDecodeWgPerCu * cus;
+    int64_t wg = (int64_t)attn::decode_wg_per_cu(d) * cus;
     if (const char* env = std::getenv("ATTN_DECODE_WORKGROUPS")) {
       const long w = std::strtol(env, nullptr, 10);
       if (w >= 1 && w <= (1 << 20)) wg = w;

@@ -14,17 +14,17 @@
 //                            across queries: a streaming dot product, so the
 //                            vector ALU is the right unit).
 //   decode_split_balanced<D, G, EXACT>  G >= 2 query heads share each KV
-//                            head, d = 64 or 128, at most 2048 sequences: the
-//                            queries form a
+//                            head, at most 2048 sequences: the queries form a
 //                            small matrix and QK^T and PV run on
 //                            v_mfma_f32_16x16x32_bf16 with the group padded to
 //                            16 columns; a persistent pass over equal units of
 //                            128 keys, with K and V staged per wave in LDS
 //                            and each wave's next copies in flight while it
-//                            computes.  decode_combine_balanced merges.
+//                            computes (two workgroups per compute unit, one
+//                            at d = 256).  decode_combine_balanced merges.
 //   decode_split_mfma<D, G, EXACT>  the same contraction on a grid of
 //                            (chunk, KV head, batch) workgroups, for larger
-//                            batches and for d = 256.
+//                            batches.
 //   EXACT: groups of exactly G = 2, 4, 8 or 16 query heads.  Otherwise any
 //   group size: each KV head's group is cut into column blocks of at most 16
 //   query heads (virtual KV heads, see GroupMap), each reading the KV head
@@ -64,29 +64,35 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 }
 
 // The score MFMA's K operand from LDS: 16-byte reads at a[ks] and a[ks] + HALF
-// (the same slots 16 rows further on) into x[0][ks] and x[1][ks], in one block
-// that waits for its own reads.  The compiler then sees no LDS read here and
-// inserts no wait for direct copies still in flight into other LDS buffers
-// (it cannot tell those buffers apart and would wait for every copy); the
-// caller waits for the copies into this buffer itself.
+// (the same slots 16 rows further on) into x0[ks] and x1[ks] for 4 k-steps,
+// in one block that waits for its own reads.  The compiler then sees no LDS
+// read here and inserts no wait for direct copies still in flight into other
+// LDS buffers (it cannot tell those buffers apart and would wait for every
+// copy); the caller waits for the copies into this buffer itself.
+template <int HALF>
+__device__ __forceinline__ void lds_read_k4(u32x4* x0, u32x4* x1, const uint32_t* a) {
+  asm volatile(
+      "ds_read_b128 %0, %8\n\t"
+      "ds_read_b128 %1, %8 offset:%12\n\t"
+      "ds_read_b128 %2, %9\n\t"
+      "ds_read_b128 %3, %9 offset:%12\n\t"
+      "ds_read_b128 %4, %10\n\t"
+      "ds_read_b128 %5, %10 offset:%12\n\t"
+      "ds_read_b128 %6, %11\n\t"
+      "ds_read_b128 %7, %11 offset:%12\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(x0[0]), "=&v"(x1[0]), "=&v"(x0[1]), "=&v"(x1[1]), "=&v"(x0[2]), "=&v"(x1[2]),
+        "=&v"(x0[3]), "=&v"(x1[3])
+      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "n"(HALF)
+      : "memory");
+}
+
 template <int KS, int HALF>
 __device__ __forceinline__ void lds_read_k(u32x4 (&x)[2][KS], const uint32_t (&a)[KS]) {
-  static_assert(KS == 2 || KS == 4, "d = 64 or 128");
-  if constexpr (KS == 4) {
-    asm volatile(
-        "ds_read_b128 %0, %8\n\t"
-        "ds_read_b128 %1, %8 offset:%12\n\t"
-        "ds_read_b128 %2, %9\n\t"
-        "ds_read_b128 %3, %9 offset:%12\n\t"
-        "ds_read_b128 %4, %10\n\t"
-        "ds_read_b128 %5, %10 offset:%12\n\t"
-        "ds_read_b128 %6, %11\n\t"
-        "ds_read_b128 %7, %11 offset:%12\n\t"
-        "s_waitcnt lgkmcnt(0)"
-        : "=&v"(x[0][0]), "=&v"(x[1][0]), "=&v"(x[0][1]), "=&v"(x[1][1]), "=&v"(x[0][2]), "=&v"(x[1][2]),
-          "=&v"(x[0][3]), "=&v"(x[1][3])
-        : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "n"(HALF)
-        : "memory");
+  static_assert(KS == 2 || KS == 4 || KS == 8, "d = 64, 128 or 256");
+  if constexpr (KS >= 4) {
+#pragma unroll
+    for (int c = 0; c < KS; c += 4) lds_read_k4<HALF>(&x[0][c], &x[1][c], &a[c]);
   } else {
     asm volatile(
         "ds_read_b128 %0, %4\n\t"
@@ -102,35 +108,41 @@ __device__ __forceinline__ void lds_read_k(u32x4 (&x)[2][KS], const uint32_t (&a
 
 // The PV MFMA's V^T operand from LDS: for output tile t, transposed 4-row
 // reads at a[t] (rows 0..15 of the step) into lo[t] and at a[t] + HALF (rows
-// 16..31) into hi[t], in one block that waits for its own reads (for the same
-// reason as lds_read_k).
+// 16..31) into hi[t], 8 tiles in one block that waits for its own reads (for
+// the same reason as lds_read_k).
+template <int HALF>
+__device__ __forceinline__ void lds_read_vt8(u32x2* lo, u32x2* hi, const uint32_t* a) {
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %16\n\t"
+      "ds_read_b64_tr_b16 %1, %16 offset:%24\n\t"
+      "ds_read_b64_tr_b16 %2, %17\n\t"
+      "ds_read_b64_tr_b16 %3, %17 offset:%24\n\t"
+      "ds_read_b64_tr_b16 %4, %18\n\t"
+      "ds_read_b64_tr_b16 %5, %18 offset:%24\n\t"
+      "ds_read_b64_tr_b16 %6, %19\n\t"
+      "ds_read_b64_tr_b16 %7, %19 offset:%24\n\t"
+      "ds_read_b64_tr_b16 %8, %20\n\t"
+      "ds_read_b64_tr_b16 %9, %20 offset:%24\n\t"
+      "ds_read_b64_tr_b16 %10, %21\n\t"
+      "ds_read_b64_tr_b16 %11, %21 offset:%24\n\t"
+      "ds_read_b64_tr_b16 %12, %22\n\t"
+      "ds_read_b64_tr_b16 %13, %22 offset:%24\n\t"
+      "ds_read_b64_tr_b16 %14, %23\n\t"
+      "ds_read_b64_tr_b16 %15, %23 offset:%24\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(lo[0]), "=&v"(hi[0]), "=&v"(lo[1]), "=&v"(hi[1]), "=&v"(lo[2]), "=&v"(hi[2]),
+        "=&v"(lo[3]), "=&v"(hi[3]), "=&v"(lo[4]), "=&v"(hi[4]), "=&v"(lo[5]), "=&v"(hi[5]),
+        "=&v"(lo[6]), "=&v"(hi[6]), "=&v"(lo[7]), "=&v"(hi[7])
+      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]), "v"(a[7]), "n"(HALF)
+      : "memory");
+}
+
 template <int DT, int HALF>
 __device__ __forceinline__ void lds_read_vt(u32x2 (&lo)[DT], u32x2 (&hi)[DT], const uint32_t (&a)[DT]) {
-  static_assert(DT == 4 || DT == 8, "d = 64 or 128");
-  if constexpr (DT == 8) {
-    asm volatile(
-        "ds_read_b64_tr_b16 %0, %16\n\t"
-        "ds_read_b64_tr_b16 %1, %16 offset:%24\n\t"
-        "ds_read_b64_tr_b16 %2, %17\n\t"
-        "ds_read_b64_tr_b16 %3, %17 offset:%24\n\t"
-        "ds_read_b64_tr_b16 %4, %18\n\t"
-        "ds_read_b64_tr_b16 %5, %18 offset:%24\n\t"
-        "ds_read_b64_tr_b16 %6, %19\n\t"
-        "ds_read_b64_tr_b16 %7, %19 offset:%24\n\t"
-        "ds_read_b64_tr_b16 %8, %20\n\t"
-        "ds_read_b64_tr_b16 %9, %20 offset:%24\n\t"
-        "ds_read_b64_tr_b16 %10, %21\n\t"
-        "ds_read_b64_tr_b16 %11, %21 offset:%24\n\t"
-        "ds_read_b64_tr_b16 %12, %22\n\t"
-        "ds_read_b64_tr_b16 %13, %22 offset:%24\n\t"
-        "ds_read_b64_tr_b16 %14, %23\n\t"
-        "ds_read_b64_tr_b16 %15, %23 offset:%24\n\t"
-        "s_waitcnt lgkmcnt(0)"
-        : "=&v"(lo[0]), "=&v"(hi[0]), "=&v"(lo[1]), "=&v"(hi[1]), "=&v"(lo[2]), "=&v"(hi[2]),
-          "=&v"(lo[3]), "=&v"(hi[3]), "=&v"(lo[4]), "=&v"(hi[4]), "=&v"(lo[5]), "=&v"(hi[5]),
-          "=&v"(lo[6]), "=&v"(hi[6]), "=&v"(lo[7]), "=&v"(hi[7])
-        : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]), "v"(a[7]), "n"(HALF)
-        : "memory");
+  static_assert(DT == 4 || DT == 8 || DT == 16, "d = 64, 128 or 256");
+  if constexpr (DT >= 8) {
+#pragma unroll
+    for (int c = 0; c < DT; c += 8) lds_read_vt8<HALF>(&lo[c], &hi[c], &a[c]);
   } else {
     asm volatile(
         "ds_read_b64_tr_b16 %0, %8\n\t"
@@ -629,7 +641,7 @@ __device__ __forceinline__ void unit_prefix(const DecodeParams& p, int hv, int* 
 }
 
 template <int D, int G, bool EXACT>
-__global__ __launch_bounds__(kThreads, kDecodeWgPerCu) void decode_split_balanced(DecodeParams p) {
+__global__ __launch_bounds__(kThreads, decode_wg_per_cu(D)) void decode_split_balanced(DecodeParams p) {
   constexpr int KS = D / 32;          // k-steps of the score MFMA (32 features each)
   constexpr int DT = D / 16;          // 16-feature output tiles
   constexpr int SLOTS = D / 8;        // 16-byte slots per V row
@@ -929,7 +941,10 @@ __global__ __launch_bounds__(64) void decode_combine_balanced(DecodeParams p) {
     for (int e = 0; e < PER; ++e) acc[e] = fmaf(wt, p.part_o[slot * D + PER * lane + e], acc[e]);
   }
   const float inv = he > hs ? 1.f / Wsum : 0.f;
-  if (PER == 2) {
+  if constexpr (PER == 4) {
+    *reinterpret_cast<u32x2*>(orow + 4 * lane) = u32x2{pack_bf16x2(acc[0] * inv, acc[1] * inv),
+                                                       pack_bf16x2(acc[2] * inv, acc[3] * inv)};
+  } else if constexpr (PER == 2) {
     reinterpret_cast<uint32_t*>(orow)[lane] = pack_bf16x2(acc[0] * inv, acc[PER - 1] * inv);
   } else {
     orow[lane] = f32_to_bf16_bits(acc[0] * inv);
@@ -984,9 +999,7 @@ hipError_t launch_balanced(const DecodeParams& p, hipStream_t stream) {
 
 template <int D, int G, bool EXACT>
 hipError_t launch_group(const DecodeParams& p, hipStream_t stream) {
-  if constexpr (D != 256) {   // the balanced pass is built for d = 64 and 128
-    if (p.n_wg > 0) return launch_balanced<D, G, EXACT>(p, stream);
-  }
+  if (p.n_wg > 0) return launch_balanced<D, G, EXACT>(p, stream);
   hipLaunchKernelGGL((decode_split_mfma<D, G, EXACT>), dim3(p.n_split, p.Hv, p.B), dim3(kThreads), 0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

@@ -76,6 +76,8 @@ constexpr int kDecodeMaxBatch = 2048;
 // (its register bound) and launched with (its persistent grid): each stages
 // a K and a V block per wave in LDS, 64 KiB per workgroup.
 constexpr int kDecodeWgPerCu = 2;
+// At d = 256 the staging doubles (128 KiB per workgroup): one per compute unit.
+constexpr int decode_wg_per_cu(int d) { return d == 256 ? 1 : kDecodeWgPerCu; }
 // Keys per work unit of the balanced decode pass (4 waves x 32 keys).
 constexpr int kDecodeUnit = 128;
 // Most workgroups of the balanced decode pass; its partials need at most

@@ -25,9 +25,10 @@ CASES = [
     (2, 8, 1, 512, 64, 128, [512, 300]),                   # d = 64, groups of 8
     (5, 4, 4, 1000, 64, 384, [1000, 999, 385, 384, 17]),   # page size 3 x 128, ragged capacity
     (3, 4, 2, 768, 64, 128, [768, 200, 1]),                # d = 64, groups of 2, a one-key cache
-    (2, 12, 4, 1280, 128, 256, [1280, 511]),               # groups of 3: vector-ALU pass per query head
+    (2, 12, 4, 1280, 128, 256, [1280, 511]),               # groups of 3 (one padded column block)
     (2, 32, 1, 640, 64, 128, [640, 129]),                  # one KV head for 32 query heads
-    (2, 4, 2, 768, 256, 256, [768, 100]),                  # d = 256
+    (2, 4, 2, 768, 256, 256, [768, 100]),                  # d = 256, groups of 2
+    (3, 16, 2, 900, 256, 128, [900, 0, 129]),              # d = 256, groups of 8
 ]
 
 
@@ -53,11 +54,12 @@ def test_paged_decode_matches_contiguous_and_oracle(case):
     assert_close(o, ref, torch.bfloat16, f"paged decode {case}")
 
 
-def test_paged_decode_large_batch_chunked_pass():
+@pytest.mark.parametrize("d", [64, 256])
+def test_paged_decode_large_batch_chunked_pass(d):
     """Query groups past the balanced pass's batch limit use the chunked split
     kernel; its steps go through the same page lookup."""
-    B, Hq, Hkv, S, d, P = 2100, 2, 1, 256, 64, 128
-    print("paged decode, chunked pass", flush=True)
+    B, Hq, Hkv, S, P = 2100, 2, 1, 256, 128
+    print(f"paged decode, chunked pass, d={d}", flush=True)
     x = wl.random_problem(B, Hq, Hkv, 1, S, d, dtype="bf16", device=DEV, seed=22)
     g = np.random.default_rng(5)
     lens = g.integers(0, S + 1, B).tolist()

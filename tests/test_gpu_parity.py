@@ -157,10 +157,13 @@ DECODE_CASES = [
     (3, 7, 1, 700, 64, [700, 1, 256]),
     (2, 32, 1, 1500, 128, [1500, 1024]),
     (4, 6, 2, 500, 128, [500, 0, 1, 257]),
-    # d = 256: every query head on the vector-ALU pass (split, unsplit, groups)
+    # d = 256: one query head per KV head on the vector-ALU pass (split and
+    # unsplit); groups of 2, 3, 16 and 20 on the balanced matrix-core pass
     (3, 4, 4, 1100, 256, [1100, 1, 0]),
     (2, 8, 4, 1300, 256, [1300, 200]),
     (2, 6, 2, 500, 256, [500, 17]),
+    (3, 16, 1, 700, 256, [700, 0, 129]),
+    (2, 40, 2, 400, 256, [31, 400]),
     # groups above 16: blocks of 10 + 10, of 9 + 8, and four blocks of 16
     (2, 40, 2, 800, 64, [800, 129]),
     (2, 17, 1, 600, 128, [600, 300]),
@@ -196,24 +199,27 @@ def test_decode_split_count_invariance(chunk, monkeypatch):
     assert_close(o, ref, torch.bfloat16, f"chunk {chunk}")
 
 
-@pytest.mark.parametrize("wgs", ["1", "3", "7", "64", "100000"])
-@pytest.mark.parametrize("Hq", [8, 6, 40], ids=["group4", "group3", "group20"])
-def test_decode_balanced_partition_invariance(wgs, Hq, monkeypatch):
+BALANCED_PARTITIONS = [(wgs, Hq, 128) for Hq in (8, 6, 40) for wgs in ("1", "3", "7", "64", "100000")]
+BALANCED_PARTITIONS += [(wgs, Hq, 256) for Hq in (8, 6) for wgs in ("1", "7", "100000")]
+
+
+@pytest.mark.parametrize("wgs,Hq,d", BALANCED_PARTITIONS, ids=lambda v: str(v))
+def test_decode_balanced_partition_invariance(wgs, Hq, d, monkeypatch):
     """Query groups: the balanced pass spreads 128-key units over a forced
     number of workgroups (one workgroup walking every head, a few, more than
     there are units); every partition merges to the oracle's result.  Lengths
     include 0 and unit boundaries, and batches with no work sit between
     others.  Groups of 4, and of 3 and 20 (column blocks of 3, and 10 + 10
-    over two virtual heads per KV head)."""
-    B, Hkv, S, d = 9, 2, 1100, 128
+    over two virtual heads per KV head); d = 128 and 256."""
+    B, Hkv, S = 9, 2, 1100
     lens = [1100, 0, 128, 129, 0, 255, 256, 1, 0]
-    say(f"decode balanced workgroups={wgs} Hq={Hq}")
+    say(f"decode balanced workgroups={wgs} Hq={Hq} d={d}")
     x = make(B, Hq, Hkv, 1, S, d, seed=15, k_mult=4.0)
     monkeypatch.setenv("ATTN_DECODE_WORKGROUPS", wgs)
     o = attn.decode(x["q"], x["k"], x["v"], kv_lens=lens_tensor(lens))
     torch.cuda.synchronize()
     ref = oracle.decode(x["q"].cpu(), x["k"].cpu(), x["v"].cpu(), lens, 1.0 / np.sqrt(d))
-    assert_close(o, ref, torch.bfloat16, f"workgroups {wgs}")
+    assert_close(o, ref, torch.bfloat16, f"workgroups {wgs} Hq {Hq} d {d}")
 
 
 def test_decode_balanced_many_batches():
@@ -231,19 +237,21 @@ def test_decode_balanced_many_batches():
     assert_close(o, ref, torch.bfloat16, "B=300")
 
 
-@pytest.mark.parametrize("Hq", [2, 3, 18], ids=["group2", "group3", "group18"])
-def test_decode_chunked_fallback_for_large_batches(Hq):
+@pytest.mark.parametrize("Hq,d", [(2, 64), (3, 64), (18, 64), (2, 256), (5, 256)],
+                         ids=["group2", "group3", "group18", "group2-d256", "group5-d256"])
+def test_decode_chunked_fallback_for_large_batches(Hq, d):
     """Past the balanced pass's batch limit query groups use the chunked
-    split pass (groups of 2; of 3 and 18 in column blocks)."""
-    B, Hkv, S, d = 2100, 1, 40, 64
+    split pass (groups of 2; of 3, 5 and 18 in column blocks; d = 64 and
+    256)."""
+    B, Hkv, S = 2100, 1, 40
     g = np.random.default_rng(10)
     lens = [int(x) for x in g.integers(0, S + 1, B)]
-    say(f"decode query groups, B=2100 Hq={Hq} (chunked pass)")
+    say(f"decode query groups, B=2100 Hq={Hq} d={d} (chunked pass)")
     x = make(B, Hq, Hkv, 1, S, d, seed=17)
     o = attn.decode(x["q"], x["k"], x["v"], kv_lens=lens_tensor(lens))
     torch.cuda.synchronize()
     ref = oracle.decode(x["q"].cpu(), x["k"].cpu(), x["v"].cpu(), lens, 1.0 / np.sqrt(d))
-    assert_close(o, ref, torch.bfloat16, f"B=2100 Hq={Hq}")
+    assert_close(o, ref, torch.bfloat16, f"B=2100 Hq={Hq} d={d}")
 
 
 # ---------------------------------------------------------------------------
