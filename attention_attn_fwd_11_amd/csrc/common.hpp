@@ -177,4 +177,59 @@ __device__ __forceinline__ float shfl(float x, int src) { return __shfl(x, src, 
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
 
+// Split-KV merge of nr partials by one wave ("Optimizing Decoder Attention
+// for LLMs on GPU", split-K decoding; the rescaling identity of "GPU learning
+// day 24: Operator Fusion", section 3.4): with M = max_r lse_r (base 2),
+//   O = sum_r 2^(lse_r - M) o_r / sum_r 2^(lse_r - M).
+// Partial r's log-sum-exp is lse[r * ls]; this lane's PER output elements of
+// it are po[r * ps + e * ES].  The lanes read the log-sum-exps in parallel and
+// reduce M and the weight sum W across the wave; the outputs are accumulated
+// 8 partials at a time with their loads issued together (a partial past nr
+// reads row nr - 1 with weight 0), so a merge of many partials is not a chain
+// of dependent loads.  Returns W (0 when nr == 0, with acc all 0).
+template <int PER, int ES>
+__device__ __forceinline__ float merge_partials(const float* lse, int64_t ls, const float* po, int64_t ps, int nr,
+                                               float (&acc)[PER]) {
+  const int lane = threadIdx.x & 63;
+  float M = kNegInf;
+  for (int r = lane; r < nr; r += 64) M = fmaxf(M, lse[(int64_t)r * ls]);
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, shfl_xor(M, o));
+#pragma unroll
+  for (int e = 0; e < PER; ++e) acc[e] = 0.f;
+  float W = 0.f;
+  for (int c = 0; c < nr; c += 64) {
+    const int r = c + lane;
+    const float w = r < nr ? exp2_fast(lse[(int64_t)r * ls] - M) : 0.f;   // weight of partial c + lane
+    W += w;
+    const int last = min(64, nr - c) - 1;
+    for (int j0 = 0; j0 <= last; j0 += 8) {
+      float v[8][PER];
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        const float* src = po + (int64_t)(c + min(j0 + t, last)) * ps;
+        if constexpr (ES == 1 && PER == 4) {
+          const float4 x = *reinterpret_cast<const float4*>(src);
+          v[t][0] = x.x; v[t][1] = x.y; v[t][2] = x.z; v[t][3] = x.w;
+        } else if constexpr (ES == 1 && PER == 2) {
+          const float2 x = *reinterpret_cast<const float2*>(src);
+          v[t][0] = x.x; v[t][1] = x.y;
+        } else {
+#pragma unroll
+          for (int e = 0; e < PER; ++e) v[t][e] = src[e * ES];
+        }
+      }
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        const float wt = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w), j0 + t));
+#pragma unroll
+        for (int e = 0; e < PER; ++e) acc[e] = fmaf(wt, v[t][e], acc[e]);
+      }
+    }
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) W += shfl_xor(W, o);
+  return W;
+}
+
 }  // namespace attn

@@ -925,22 +925,15 @@ __global__ __launch_bounds__(64) void decode_combine_balanced(DecodeParams p) {
   const int hs = before * HV + g * units_b, he = hs + units_b;
   uint16_t* orow = static_cast<uint16_t*>(p.o) + ((int64_t)b * p.Hq + hq) * D;
   constexpr int PER = D / 64;
+  // The head's runs start at hs and at every multiple of R inside (hs, he),
+  // so their slots run_slot(head, s, R) are consecutive: head + hs/R ..
+  // head + (he-1)/R.
+  const int nr = he > hs ? (he - 1) / R - hs / R + 1 : 0;
+  const int64_t slot0 = (int64_t)run_slot(b * HV + g, hs, R) * CB + qi;
   float acc[PER];
-#pragma unroll
-  for (int e = 0; e < PER; ++e) acc[e] = 0.f;
-  float M = kNegInf;
-  const int head = b * HV + g;
-  for (int s = hs; s < he; s = (s / R + 1) * R)
-    M = fmaxf(M, p.part_lse[(int64_t)run_slot(head, s, R) * CB + qi]);
-  float Wsum = 0.f;
-  for (int s = hs; s < he; s = (s / R + 1) * R) {
-    const int64_t slot = (int64_t)run_slot(head, s, R) * CB + qi;
-    const float wt = exp2_fast(p.part_lse[slot] - M);
-    Wsum += wt;
-#pragma unroll
-    for (int e = 0; e < PER; ++e) acc[e] = fmaf(wt, p.part_o[slot * D + PER * lane + e], acc[e]);
-  }
-  const float inv = he > hs ? 1.f / Wsum : 0.f;
+  const float Wsum = merge_partials<PER, 1>(p.part_lse + slot0, CB, p.part_o + slot0 * D + PER * lane,
+                                            (int64_t)CB * D, nr, acc);
+  const float inv = nr > 0 ? 1.f / Wsum : 0.f;
   if constexpr (PER == 4) {
     *reinterpret_cast<u32x2*>(orow + 4 * lane) = u32x2{pack_bf16x2(acc[0] * inv, acc[1] * inv),
                                                        pack_bf16x2(acc[2] * inv, acc[3] * inv)};
@@ -965,17 +958,7 @@ __global__ __launch_bounds__(64) void decode_combine(DecodeParams p) {
   const int64_t prow0 = ((int64_t)b * p.Hq + h) * p.n_split;
   constexpr int PER = D / 64;
   float acc[PER];
-#pragma unroll
-  for (int e = 0; e < PER; ++e) acc[e] = 0.f;
-  float M = kNegInf;
-  for (int s = 0; s < ns; ++s) M = fmaxf(M, p.part_lse[prow0 + s]);
-  float W = 0.f;
-  for (int s = 0; s < ns; ++s) {
-    const float wt = exp2_fast(p.part_lse[prow0 + s] - M);
-    W += wt;
-#pragma unroll
-    for (int e = 0; e < PER; ++e) acc[e] = fmaf(wt, p.part_o[(prow0 + s) * D + PER * lane + e], acc[e]);
-  }
+  const float W = merge_partials<PER, 1>(p.part_lse + prow0, 1, p.part_o + prow0 * D + PER * lane, D, ns, acc);
   const float inv = ns > 0 ? 1.f / W : 0.f;
   if constexpr (PER == 4) {
     *reinterpret_cast<u32x2*>(orow + 4 * lane) = u32x2{pack_bf16x2(acc[0] * inv, acc[1] * inv),

@@ -173,18 +173,8 @@ __global__ __launch_bounds__(64) void decode_combine_f32(DecodeParams p) {
   const int ns = (n + p.chunk - 1) / p.chunk;
   float* orow = static_cast<float*>(p.o) + ((int64_t)b * p.Hq + h) * D;
   const int64_t prow0 = ((int64_t)b * p.Hq + h) * p.n_split;
-  float M = kNegInf;
-  for (int s = 0; s < ns; ++s) M = fmaxf(M, p.part_lse[prow0 + s]);
-  float W = 0.f;
   float acc[D / 64];
-#pragma unroll
-  for (int e = 0; e < D / 64; ++e) acc[e] = 0.f;
-  for (int s = 0; s < ns; ++s) {
-    const float wt = exp2_fast(p.part_lse[prow0 + s] - M);
-    W += wt;
-#pragma unroll
-    for (int e = 0; e < D / 64; ++e) acc[e] = fmaf(wt, p.part_o[(prow0 + s) * D + lane + 64 * e], acc[e]);
-  }
+  const float W = merge_partials<D / 64, 64>(p.part_lse + prow0, 1, p.part_o + prow0 * D + lane, D, ns, acc);
 #pragma unroll
   for (int e = 0; e < D / 64; ++e) orow[lane + 64 * e] = ns > 0 ? acc[e] / W : 0.f;
 }

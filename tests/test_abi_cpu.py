@@ -225,27 +225,51 @@ def test_workspace_bytes(lib):
     assert ws(2, 4, 1, 100, 64) >= 2 * 4 * (64 + 1) * 4
 
 
+@pytest.mark.parametrize("B,H,S,splits", [
+    (64, 32, 4096, 2),     # 2048 heads: two splits (about 4096 workgroups)
+    (128, 32, 4096, 1),    # 4096 heads: one
+    (16, 32, 8192, 8),     # 512 heads
+    (4, 32, 8192, 16),     # 128 heads: capped at 512 keys per split
+    (1, 32, 4096, 8),
+    (1, 32, 32768, 64),
+])
+def test_workspace_split_policy(lib, B, H, S, splits):
+    """One query head per KV head: the workspace holds exactly the chosen
+    splits' partials, B * H * splits rows of d + 1 floats (each part padded
+    to 256 bytes); about 4096 workgroups, never below 512 keys per split."""
+    rows = B * H * splits
+    pad = lambda x: (x + 255) // 256 * 256
+    assert attn.attn_decode_workspace_bytes(B, H, H, S, 128) == pad(rows * 128 * 4) + pad(rows * 4)
+
+
 def test_workspace_head_dim_256(lib):
-    """d = 256 decodes (every group on the vector-ALU pass over query heads):
-    a partial of 256 + 1 floats per split and query head."""
+    """d = 256 decodes: partials of 256 + 1 floats, per split and query head
+    on the vector-ALU pass (one query head per KV head), per run and query
+    head on the balanced pass (query groups)."""
     ws = attn.attn_decode_workspace_bytes
-    # B4 H_q16 H_kv8: 64 query heads -> 8 splits of 512 keys for 4096 keys
-    assert ws(4, 16, 8, 4096, 256) >= 4 * 16 * 8 * (256 + 1) * 4
+    # B4 H16: 64 heads -> 8 splits of 512 keys for 4096 keys
+    assert ws(4, 16, 16, 4096, 256) >= 4 * 16 * 8 * (256 + 1) * 4
+    # B4 H_q16 H_kv8: 4 * 8 heads of 32 units -> 1024 workgroups, (32 + 1024)
+    # runs of 2 query heads
+    assert ws(4, 16, 8, 4096, 256) >= (4 * 8 + 1024) * 2 * (256 + 1) * 4
     assert ws(1, 32, 32, 4096, 96) == 0
 
 
 def test_workspace_other_group_sizes(lib, monkeypatch):
-    """Group sizes the matrix-core kernels do not take (7, 32, 3) run the
-    vector-ALU split per query head: a partial per split and query head,
-    the split count aiming at about 4096 workgroups of (split, query head,
-    batch) and never below 512 keys per split."""
+    """Group sizes other than 2, 4, 8 and 16 run the balanced pass in column
+    blocks of at most 16 query heads (virtual KV heads): a partial per run
+    and column of a block, fewer than (virtual heads + workgroups) runs."""
     ws = attn.attn_decode_workspace_bytes
-    # B2 H_q28 H_kv4: 56 query heads -> 8 splits of 512 keys for 4096 keys
-    assert ws(2, 28, 4, 4096, 128) >= 2 * 28 * 8 * (128 + 1) * 4
-    # B4 H_q32 H_kv1 (one KV head): 128 query heads -> 4 splits of 512 for 2048 keys
-    assert ws(4, 32, 1, 2048, 64) >= 4 * 32 * 4 * (64 + 1) * 4
+    # B2 H_q28 H_kv4 (groups of 7, one block each): 2 * 4 heads of 32 units
+    # -> 256 workgroups, (8 + 256) runs of 7 query heads
+    assert ws(2, 28, 4, 4096, 128) >= (8 + 256) * 7 * (128 + 1) * 4
+    # B4 H_q32 H_kv1 (one KV head, two blocks of 16): 4 * 2 virtual heads of
+    # 16 units -> 128 workgroups, (8 + 128) runs of 16 query heads
+    assert ws(4, 32, 1, 2048, 64) >= (8 + 128) * 16 * (64 + 1) * 4
+    # the chunk override is for the chunked pass only
+    base = ws(1, 3, 1, 1024, 128)
     monkeypatch.setenv("ATTN_DECODE_CHUNK", "256")
-    assert ws(1, 3, 1, 1024, 128) >= 1 * 3 * 4 * (128 + 1) * 4
+    assert ws(1, 3, 1, 1024, 128) == base
 
 
 def test_workspace_follows_chunk_override(lib, monkeypatch):

@@ -69,12 +69,14 @@ def test_decode_f32_matches_oracle(case):
         assert torch.all(o[[i for i, n in enumerate(lens) if n == 0]] == 0)
 
 
-@pytest.mark.parametrize("chunk", ["256", "768"])
-def test_decode_f32_split_count_invariance(chunk, monkeypatch):
+@pytest.mark.parametrize("chunk,S,lens", [("256", 2000, [2000, 1300]), ("768", 2000, [2000, 1300]),
+                                          ("256", 20000, [20000, 8321])])
+def test_decode_f32_split_count_invariance(chunk, S, lens, monkeypatch):
     """Forced chunk sizes (several partials per head, a ragged last one) merge
-    to the oracle's result."""
-    B, Hq, Hkv, S, d, lens = 2, 4, 2, 2000, 128, [2000, 1300]
-    say(f"fp32 decode, chunk {chunk}")
+    to the oracle's result; 79 and 33 partials per head in the last case
+    (more than a wave's 64 lanes)."""
+    B, Hq, Hkv, d = 2, 4, 2, 128
+    say(f"fp32 decode, chunk {chunk}, S {S}")
     monkeypatch.setenv("ATTN_DECODE_CHUNK", chunk)
     x = wl.random_problem(B, Hq, Hkv, 1, S, d, dtype="f32", device=DEV, seed=32)
     lt = torch.tensor(lens, dtype=torch.int32, device=DEV)

@@ -237,6 +237,27 @@ def test_decode_balanced_many_batches():
     assert_close(o, ref, torch.bfloat16, "B=300")
 
 
+@pytest.mark.parametrize("Hq,Hkv,chunk,wgs", [(4, 4, "256", None), (8, 2, None, "100000"), (6, 2, None, "100000")],
+                         ids=["mha-79-splits", "group4-157-runs", "group3-157-runs"])
+def test_decode_merge_of_many_partials(Hq, Hkv, chunk, wgs, monkeypatch):
+    """Heads with more partials than a wave has lanes (the combine merges them
+    64 at a time, 8 loads in flight): 256-key chunks of a 20000-key cache
+    (79 splits), and one balanced run per 128-key unit (157 runs; ragged
+    lengths give 66 and 65)."""
+    B, S, D = 3, 20000, 128
+    lens = [20000, 8321, 8193]
+    if chunk:
+        monkeypatch.setenv("ATTN_DECODE_CHUNK", chunk)
+    if wgs:
+        monkeypatch.setenv("ATTN_DECODE_WORKGROUPS", wgs)
+    say(f"decode many partials Hq={Hq} Hkv={Hkv} chunk={chunk} workgroups={wgs}")
+    x = make(B, Hq, Hkv, 1, S, D, seed=18, k_mult=4.0)
+    o = attn.decode(x["q"], x["k"], x["v"], kv_lens=lens_tensor(lens))
+    torch.cuda.synchronize()
+    ref = oracle.decode(x["q"].cpu(), x["k"].cpu(), x["v"].cpu(), lens, 1.0 / np.sqrt(D))
+    assert_close(o, ref, torch.bfloat16, f"many partials Hq={Hq} Hkv={Hkv}")
+
+
 @pytest.mark.parametrize("Hq,d", [(2, 64), (3, 64), (18, 64), (2, 256), (5, 256)],
                          ids=["group2", "group3", "group18", "group2-d256", "group5-d256"])
 def test_decode_chunked_fallback_for_large_batches(Hq, d):
