@@ -177,37 +177,45 @@ __device__ __forceinline__ float shfl(float x, int src) { return __shfl(x, src, 
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
 
-// Split-KV merge of nr partials by one wave ("Optimizing Decoder Attention
-// for LLMs on GPU", split-K decoding; the rescaling identity of "GPU learning
-// day 24: Operator Fusion", section 3.4): with M = max_r lse_r (base 2),
+// Split-KV merge ("Optimizing Decoder Attention for LLMs on GPU", split-K
+// decoding; the rescaling identity of "GPU learning day 24: Operator Fusion",
+// section 3.4): with M = max_r lse_r (base 2),
 //   O = sum_r 2^(lse_r - M) o_r / sum_r 2^(lse_r - M).
 // Partial r's log-sum-exp is lse[r * ls]; this lane's PER output elements of
-// it are po[r * ps + e * ES].  The lanes read the log-sum-exps in parallel and
-// reduce M and the weight sum W across the wave; the outputs are accumulated
-// 8 partials at a time with their loads issued together (a partial past nr
-// reads row nr - 1 with weight 0), so a merge of many partials is not a chain
-// of dependent loads.  Returns W (0 when nr == 0, with acc all 0).
+// it are po[r * ps + e * ES].
+constexpr int kMergeBatch = 16;   // partials whose output loads are issued together
+constexpr int kMergeWaves = 4;    // waves of a combine workgroup
+
+// One wave over partials 0 .. nr-1: M, the weight sum W = sum_r 2^(lse_r - M)
+// and acc = sum_r 2^(lse_r - M) o_r (M = -inf, W = 0, acc = 0 when nr == 0).
+// The lanes read the log-sum-exps in parallel and reduce M and W across the
+// wave; the outputs are accumulated kMergeBatch partials at a time with their
+// loads issued together (the loads past nr are skipped and their weights are
+// 0), so a merge of many partials is not a chain of dependent loads.
 template <int PER, int ES>
-__device__ __forceinline__ float merge_partials(const float* lse, int64_t ls, const float* po, int64_t ps, int nr,
-                                               float (&acc)[PER]) {
+__device__ __forceinline__ void merge_range(const float* lse, int64_t ls, const float* po, int64_t ps, int nr,
+                                            float& M, float& W, float (&acc)[PER]) {
   const int lane = threadIdx.x & 63;
-  float M = kNegInf;
+  M = kNegInf;
   for (int r = lane; r < nr; r += 64) M = fmaxf(M, lse[(int64_t)r * ls]);
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, shfl_xor(M, o));
 #pragma unroll
   for (int e = 0; e < PER; ++e) acc[e] = 0.f;
-  float W = 0.f;
+  W = 0.f;
   for (int c = 0; c < nr; c += 64) {
     const int r = c + lane;
     const float w = r < nr ? exp2_fast(lse[(int64_t)r * ls] - M) : 0.f;   // weight of partial c + lane
     W += w;
     const int last = min(64, nr - c) - 1;
-    for (int j0 = 0; j0 <= last; j0 += 8) {
-      float v[8][PER];
+    for (int j0 = 0; j0 <= last; j0 += kMergeBatch) {
+      float v[kMergeBatch][PER];
 #pragma unroll
-      for (int t = 0; t < 8; ++t) {
-        const float* src = po + (int64_t)(c + min(j0 + t, last)) * ps;
+      for (int t = 0; t < kMergeBatch; ++t) {
+#pragma unroll
+        for (int e = 0; e < PER; ++e) v[t][e] = 0.f;
+        if (j0 + t > last) continue;   // uniform across the wave
+        const float* src = po + (int64_t)(c + j0 + t) * ps;
         if constexpr (ES == 1 && PER == 4) {
           const float4 x = *reinterpret_cast<const float4*>(src);
           v[t][0] = x.x; v[t][1] = x.y; v[t][2] = x.z; v[t][3] = x.w;
@@ -220,7 +228,7 @@ __device__ __forceinline__ float merge_partials(const float* lse, int64_t ls, co
         }
       }
 #pragma unroll
-      for (int t = 0; t < 8; ++t) {
+      for (int t = 0; t < kMergeBatch; ++t) {
         const float wt = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w), j0 + t));
 #pragma unroll
         for (int e = 0; e < PER; ++e) acc[e] = fmaf(wt, v[t][e], acc[e]);
@@ -229,7 +237,55 @@ __device__ __forceinline__ float merge_partials(const float* lse, int64_t ls, co
   }
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) W += shfl_xor(W, o);
-  return W;
+}
+
+template <int PER, int NW>
+struct MergeShared {
+  float m[NW];
+  float w[NW];
+  float acc[NW][PER][64];
+};
+
+// A combine workgroup of NW waves (1 or kMergeWaves) merges nr partials:
+// with one wave, or below 64 partials, wave 0 alone; otherwise each wave a
+// contiguous share (at least 16 partials), the shares joined by the same
+// identity through LDS.  nr must be the same for the whole workgroup.
+// Returns the weight sum W relative to the overall maximum and leaves acc in
+// wave 0's lanes (O = acc / W; W = 0 when nr == 0); the other waves' results
+// are not meaningful.
+template <int PER, int ES, int NW>
+__device__ __forceinline__ float merge_partials(const float* lse, int64_t ls, const float* po, int64_t ps, int nr,
+                                               float (&acc)[PER], MergeShared<PER, NW>& sh) {
+  const int wave = NW == 1 ? 0 : threadIdx.x >> 6, lane = threadIdx.x & 63;
+  float M, W;
+  if (NW == 1 || nr < 64) {
+    merge_range<PER, ES>(lse, ls, po, ps, wave == 0 ? nr : 0, M, W, acc);
+    return W;
+  }
+  const int r0 = (int)((int64_t)nr * wave / NW);
+  const int r1 = (int)((int64_t)nr * (wave + 1) / NW);
+  merge_range<PER, ES>(lse + r0 * ls, ls, po + r0 * ps, ps, r1 - r0, M, W, acc);
+  if (lane == 0) {
+    sh.m[wave] = M;
+    sh.w[wave] = W;
+  }
+#pragma unroll
+  for (int e = 0; e < PER; ++e) sh.acc[wave][e][lane] = acc[e];
+  __syncthreads();
+  float Mt = sh.m[0];
+#pragma unroll
+  for (int w = 1; w < NW; ++w) Mt = fmaxf(Mt, sh.m[w]);
+  float Wt = 0.f;
+#pragma unroll
+  for (int e = 0; e < PER; ++e) acc[e] = 0.f;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    const float sc = exp2_fast(sh.m[w] - Mt);
+    Wt = fmaf(sc, sh.w[w], Wt);
+#pragma unroll
+    for (int e = 0; e < PER; ++e) acc[e] = fmaf(sc, sh.acc[w][e][lane], acc[e]);
+  }
+  return Wt;
 }
 
 }  // namespace attn

@@ -21,7 +21,8 @@
 //                            128 keys, with K and V staged per wave in LDS
 //                            and each wave's next copies in flight while it
 //                            computes (two workgroups per compute unit, one
-//                            at d = 256).  decode_combine_balanced merges.
+//                            at d = 256).  decode_combine_balanced<D, G,
+//                            EXACT, NW> merges.
 //   decode_split_mfma<D, G, EXACT>  the same contraction on a grid of
 //                            (chunk, KV head, batch) workgroups, for larger
 //                            batches.
@@ -29,8 +30,10 @@
 //   group size: each KV head's group is cut into column blocks of at most 16
 //   query heads (virtual KV heads, see GroupMap), each reading the KV head
 //   once, and G is the padded capacity (4, 8 or 16) of a block.
-//   decode_combine<D>        merges the partials of one (batch, query head);
-//                            not launched when every head has a single split
+//   decode_combine<D, NW>    merges the partials of one (batch, query head)
+//                            with NW = 1 or 4 waves (four share the partials
+//                            of heads that may have more than 64); not
+//                            launched when every head has a single split
 //                            (decode_split_valu then writes O itself).
 //
 // Partial results are fp32; the log-sum-exp is kept in base-2 units
@@ -889,10 +892,11 @@ __global__ __launch_bounds__(kThreads, decode_wg_per_cu(D)) void decode_split_ba
 
 // Combine for the balanced pass: (virtual) head (b, g) owns units [hs, he);
 // its segments start at hs and at every multiple of R inside (hs, he).
-template <int D, int G, bool EXACT>
-__global__ __launch_bounds__(64) void decode_combine_balanced(DecodeParams p) {
+template <int D, int G, bool EXACT, int NW>
+__global__ __launch_bounds__(64 * NW) void decode_combine_balanced(DecodeParams p) {
+  __shared__ MergeShared<D / 64, NW> sh;
   const int hq = blockIdx.x, b = blockIdx.y;
-  const int lane = threadIdx.x;
+  const int lane = threadIdx.x & 63;
   const int HV = EXACT ? p.Hkv : p.Hv;
   const int CB = EXACT ? G : p.cb;
   int g, qi;                            // virtual KV head, column within its block
@@ -931,8 +935,9 @@ __global__ __launch_bounds__(64) void decode_combine_balanced(DecodeParams p) {
   const int nr = he > hs ? (he - 1) / R - hs / R + 1 : 0;
   const int64_t slot0 = (int64_t)run_slot(b * HV + g, hs, R) * CB + qi;
   float acc[PER];
-  const float Wsum = merge_partials<PER, 1>(p.part_lse + slot0, CB, p.part_o + slot0 * D + PER * lane,
-                                            (int64_t)CB * D, nr, acc);
+  const float Wsum = merge_partials<PER, 1, NW>(p.part_lse + slot0, CB, p.part_o + slot0 * D + PER * lane,
+                                                (int64_t)CB * D, nr, acc, sh);
+  if (threadIdx.x >= 64) return;   // wave 0 holds the result
   const float inv = nr > 0 ? 1.f / Wsum : 0.f;
   if constexpr (PER == 4) {
     *reinterpret_cast<u32x2*>(orow + 4 * lane) = u32x2{pack_bf16x2(acc[0] * inv, acc[1] * inv),
@@ -947,10 +952,11 @@ __global__ __launch_bounds__(64) void decode_combine_balanced(DecodeParams p) {
 // ---------------------------------------------------------------------------
 // Combine: O = sum_s 2^(lse_s - M) o_s / sum_s 2^(lse_s - M), M = max_s lse_s.
 // ---------------------------------------------------------------------------
-template <int D>
-__global__ __launch_bounds__(64) void decode_combine(DecodeParams p) {
+template <int D, int NW>
+__global__ __launch_bounds__(64 * NW) void decode_combine(DecodeParams p) {
+  __shared__ MergeShared<D / 64, NW> sh;
   const int h = blockIdx.x, b = blockIdx.y;
-  const int lane = threadIdx.x;
+  const int lane = threadIdx.x & 63;
   int n = p.Skv;
   if (p.kv_lens) n = min(max(p.kv_lens[b], 0), p.Skv);
   const int ns = (n + p.chunk - 1) / p.chunk;
@@ -958,7 +964,8 @@ __global__ __launch_bounds__(64) void decode_combine(DecodeParams p) {
   const int64_t prow0 = ((int64_t)b * p.Hq + h) * p.n_split;
   constexpr int PER = D / 64;
   float acc[PER];
-  const float W = merge_partials<PER, 1>(p.part_lse + prow0, 1, p.part_o + prow0 * D + PER * lane, D, ns, acc);
+  const float W = merge_partials<PER, 1, NW>(p.part_lse + prow0, 1, p.part_o + prow0 * D + PER * lane, D, ns, acc, sh);
+  if (threadIdx.x >= 64) return;   // wave 0 holds the result
   const float inv = ns > 0 ? 1.f / W : 0.f;
   if constexpr (PER == 4) {
     *reinterpret_cast<u32x2*>(orow + 4 * lane) = u32x2{pack_bf16x2(acc[0] * inv, acc[1] * inv),
@@ -970,13 +977,33 @@ __global__ __launch_bounds__(64) void decode_combine(DecodeParams p) {
   }
 }
 
+// Combine workgroups: kMergeWaves waves when a head may have more than 64
+// partials (the waves share them), else one.  The chunked passes know their
+// split count.  The balanced pass's runs per head are at most its units per
+// head, ceil(S_kv / kDecodeUnit), and are few whenever many heads share the
+// grid, so it takes four waves only for long caches over at most 1024 query
+// heads (four waves per head cost a few µs over 4096 heads).
+template <int D>
+hipError_t launch_combine(const DecodeParams& p, hipStream_t stream) {
+  if (p.n_split >= 64)
+    hipLaunchKernelGGL((decode_combine<D, kMergeWaves>), dim3(p.Hq, p.B), dim3(64 * kMergeWaves), 0, stream, p);
+  else
+    hipLaunchKernelGGL((decode_combine<D, 1>), dim3(p.Hq, p.B), dim3(64), 0, stream, p);
+  return hipGetLastError();
+}
+
 template <int D, int G, bool EXACT>
 hipError_t launch_balanced(const DecodeParams& p, hipStream_t stream) {
   hipLaunchKernelGGL((decode_split_balanced<D, G, EXACT>), dim3(p.n_wg), dim3(kThreads), (p.B + 1) * sizeof(int),
                      stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((decode_combine_balanced<D, G, EXACT>), dim3(p.Hq, p.B), dim3(64), 0, stream, p);
+  const bool wide = (p.Skv + kDecodeUnit - 1) / kDecodeUnit > 64 && (int64_t)p.B * p.Hq <= 1024;
+  if (wide)
+    hipLaunchKernelGGL((decode_combine_balanced<D, G, EXACT, kMergeWaves>), dim3(p.Hq, p.B), dim3(64 * kMergeWaves),
+                       0, stream, p);
+  else
+    hipLaunchKernelGGL((decode_combine_balanced<D, G, EXACT, 1>), dim3(p.Hq, p.B), dim3(64), 0, stream, p);
   return hipGetLastError();
 }
 
@@ -986,8 +1013,7 @@ hipError_t launch_group(const DecodeParams& p, hipStream_t stream) {
   hipLaunchKernelGGL((decode_split_mfma<D, G, EXACT>), dim3(p.n_split, p.Hv, p.B), dim3(kThreads), 0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((decode_combine<D>), dim3(p.Hq, p.B), dim3(64), 0, stream, p);
-  return hipGetLastError();
+  return launch_combine<D>(p, stream);
 }
 
 template <int D>
@@ -997,8 +1023,7 @@ hipError_t launch_d(const DecodeParams& p, hipStream_t stream) {
     hipLaunchKernelGGL((decode_split_valu<D>), dim3(p.n_split, p.Hq, p.B), dim3(kThreads), 0, stream, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || p.n_split == 1) return e;   // one split: the split pass wrote O
-    hipLaunchKernelGGL((decode_combine<D>), dim3(p.Hq, p.B), dim3(64), 0, stream, p);
-    return hipGetLastError();
+    return launch_combine<D>(p, stream);
   }
   {
   if (p.kv_div == 1 && p.cb == G) {

@@ -14,8 +14,9 @@
 //                          cores; with query groups each query head streams
 //                          its KV head's rows itself, so K/V is read once
 //                          per query head, mostly from L2 for the later ones).
-//   decode_combine_f32<D>  merges a head's partials into O (skipped when
-//                          every head has a single split).
+//   decode_combine_f32<D, NW>  merges a head's partials into O with one
+//                          wave, or four that share 64 or more partials
+//                          (skipped when every head has a single split).
 //
 // Partials share the bf16 decode's workspace layout of its chunked pass:
 // part_o [B, Hq, n_split, d] normalised, part_lse [B, Hq, n_split] in base 2.
@@ -164,17 +165,19 @@ __global__ __launch_bounds__(kThreads) void decode_split_f32(DecodeParams p) {
 }
 
 // Merge of a head's partials: the splits that start below the length.
-template <int D>
-__global__ __launch_bounds__(64) void decode_combine_f32(DecodeParams p) {
+template <int D, int NW>
+__global__ __launch_bounds__(64 * NW) void decode_combine_f32(DecodeParams p) {
+  __shared__ MergeShared<D / 64, NW> sh;
   const int h = blockIdx.x, b = blockIdx.y;
-  const int lane = threadIdx.x;
+  const int lane = threadIdx.x & 63;
   int n = p.Skv;
   if (p.kv_lens) n = min(max(p.kv_lens[b], 0), p.Skv);
   const int ns = (n + p.chunk - 1) / p.chunk;
   float* orow = static_cast<float*>(p.o) + ((int64_t)b * p.Hq + h) * D;
   const int64_t prow0 = ((int64_t)b * p.Hq + h) * p.n_split;
   float acc[D / 64];
-  const float W = merge_partials<D / 64, 64>(p.part_lse + prow0, 1, p.part_o + prow0 * D + lane, D, ns, acc);
+  const float W = merge_partials<D / 64, 64, NW>(p.part_lse + prow0, 1, p.part_o + prow0 * D + lane, D, ns, acc, sh);
+  if (threadIdx.x >= 64) return;   // wave 0 holds the result
 #pragma unroll
   for (int e = 0; e < D / 64; ++e) orow[lane + 64 * e] = ns > 0 ? acc[e] / W : 0.f;
 }
@@ -184,7 +187,11 @@ hipError_t launch_d(const DecodeParams& p, hipStream_t stream) {
   hipLaunchKernelGGL((decode_split_f32<D>), dim3(p.n_split, p.Hq, p.B), dim3(kThreads), 0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.n_split == 1) return e;
-  hipLaunchKernelGGL((decode_combine_f32<D>), dim3(p.Hq, p.B), dim3(64), 0, stream, p);
+  // four waves share a head's partials when there may be 64 or more
+  if (p.n_split >= 64)
+    hipLaunchKernelGGL((decode_combine_f32<D, kMergeWaves>), dim3(p.Hq, p.B), dim3(64 * kMergeWaves), 0, stream, p);
+  else
+    hipLaunchKernelGGL((decode_combine_f32<D, 1>), dim3(p.Hq, p.B), dim3(64), 0, stream, p);
   return hipGetLastError();
 }
 

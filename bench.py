@@ -681,7 +681,7 @@ def main():
     roof_d = {"bound": "hbm", "achieved": round(gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
               "frac": round(gbps / PEAK_HBM_GBPS, 4),
               "traffic": measured_traffic(wd.name, "decode"), "traffic_unit": "bytes/launch",
-              "kernel": "decode_split_valu<128> + decode_combine<128>",
+              "kernel": "decode_split_valu<128> + decode_combine<128, 1>",
               "avg_launch_ms": round(ms_d, 4), "algorithmic_per_launch": bytes_d}
     dominant, second = (roof_p, roof_d) if ms_p >= ms_d else (roof_d, roof_p)
 

@@ -240,12 +240,13 @@ def test_decode_balanced_many_batches():
 @pytest.mark.parametrize("Hq,Hkv,chunk,wgs", [(4, 4, "256", None), (8, 2, None, "100000"), (6, 2, None, "100000")],
                          ids=["mha-79-splits", "group4-157-runs", "group3-157-runs"])
 def test_decode_merge_of_many_partials(Hq, Hkv, chunk, wgs, monkeypatch):
-    """Heads with more partials than a wave has lanes (the combine merges them
-    64 at a time, 8 loads in flight): 256-key chunks of a 20000-key cache
-    (79 splits), and one balanced run per 128-key unit (157 runs; ragged
-    lengths give 66 and 65)."""
-    B, S, D = 3, 20000, 128
-    lens = [20000, 8321, 8193]
+    """Heads with more partials than a wave has lanes (four waves share them,
+    each merging 64 at a time with 16 loads in flight): 256-key chunks of a
+    20000-key cache (79 splits), and one balanced run per 128-key unit (157
+    runs; ragged lengths give 66 and 65; short and empty sequences in the
+    same launch take the one-wave merge)."""
+    B, S, D = 5, 20000, 128
+    lens = [20000, 8321, 8193, 300, 0]
     if chunk:
         monkeypatch.setenv("ATTN_DECODE_CHUNK", chunk)
     if wgs:
