@@ -78,6 +78,8 @@ WORKLOADS = [
              "bf16", True, len_range=(512, 8192),
              note="chunked prefill: 512 new tokens per sequence over a ragged KV cache "
                   "(bottom-right causal)"),
+    Workload("decode_gqa_long_bf16_b1h32kv8l131072", "decode", 1, 32, 8, 1, 131072, 128, "bf16",
+             False, note="long-context GQA decode: one sequence of 131072 keys"),
 ]
 BY_NAME = {w.name: w for w in WORKLOADS}
 

@@ -177,7 +177,7 @@ def cpu_baseline(wl, seconds, inputs=None):
     """The fp64 oracle timed on this host's cores for every configuration, in
     the unit of its GPU figure: TFLOP/s for prefill (algorithmic FLOPs, 4*d
     per visible pair), GB/s for decode (K+V bytes of every visible row).
-    The fp32 prefill and both decodes are evaluated in full; the two large
+    The fp32 prefill and the three decodes are evaluated in full; the two large
     prefills on random query rows, about `seconds` each.  The headline
     prefill's entry is the top-level figure.  Where the GPU output of the
     same inputs is at hand (the benchmark's last call), `parity` gives its
@@ -218,7 +218,8 @@ def cpu_baseline(wl, seconds, inputs=None):
     f1 = wl.prefill_flops(w1)
     per[w1.name] = {"value": f1 / t1 / 1e9, "unit": "GFLOP/s", "seconds_per_call": t1,
                     "sample": "whole output (fp32 inputs)", "parity": e1}
-    for name in ("decode_bf16_b64h32l4096", "decode_gqa_bf16_b128h32kv8"):
+    for name in ("decode_bf16_b64h32l4096", "decode_gqa_bf16_b128h32kv8",
+                 "decode_gqa_long_bf16_b1h32kv8l131072"):
         w = wl.BY_NAME[name]
         x, t, err = full(w, 0.0)
         by = wl.decode_kv_bytes(w, x["kv_lens"])
@@ -615,7 +616,8 @@ def main():
     others = [] if args.no_others else [wl.BY_NAME[n] for n in (
         "decode_gqa_bf16_b128h32kv8", "prefill_gqa_bf16_h64kv8s16384",
         "prefill_bf16_b4h32s4096_d64", "prefill_bf16_b4h16s4096_d256",
-        "prefill_chunked_gqa_bf16_b16h32kv8q512", "prefill_noncausal_bf16_b4h32s4096")]
+        "prefill_chunked_gqa_bf16_b16h32kv8q512", "prefill_noncausal_bf16_b4h32s4096",
+        "decode_gqa_long_bf16_b1h32kv8l131072")]
     inputs = {w.name: wl.generate(w, dev) for w in [wp, wd, *others]}
     torch.cuda.synchronize()
 

@@ -79,7 +79,8 @@ def test_prefill_whole_output(name):
     check_whole(o, ref, name)
 
 
-@pytest.mark.parametrize("name", ["decode_bf16_b64h32l4096", "decode_gqa_bf16_b128h32kv8"])
+@pytest.mark.parametrize("name", ["decode_bf16_b64h32l4096", "decode_gqa_bf16_b128h32kv8",
+                                  "decode_gqa_long_bf16_b1h32kv8l131072"])
 def test_decode_whole_output(name):
     w = wl.BY_NAME[name]
     say(f"whole output {name}: {w.describe()}")
