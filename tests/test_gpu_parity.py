@@ -237,16 +237,28 @@ def test_decode_balanced_many_batches():
     assert_close(o, ref, torch.bfloat16, "B=300")
 
 
-@pytest.mark.parametrize("Hq,Hkv,chunk,wgs", [(4, 4, "256", None), (8, 2, None, "100000"), (6, 2, None, "100000")],
-                         ids=["mha-79-splits", "group4-157-runs", "group3-157-runs"])
-def test_decode_merge_of_many_partials(Hq, Hkv, chunk, wgs, monkeypatch):
+MANY_PARTIALS = [
+    # Hq, Hkv, forced chunk, forced workgroups, S, lens
+    (4, 4, "256", None, 20000, [20000, 8321, 8193, 300, 0]),
+    (8, 2, None, "100000", 20000, [20000, 8321, 8193, 300, 0]),
+    (6, 2, None, "100000", 20000, [20000, 8321, 8193, 300, 0]),
+    # at the four-wave threshold: 64 and 63 partials per head
+    (4, 4, "256", None, 16384, [16384, 16128, 16129]),
+    (8, 2, None, "100000", 8320, [8192, 8064, 8193]),
+]
+
+
+@pytest.mark.parametrize("Hq,Hkv,chunk,wgs,S,lens", MANY_PARTIALS,
+                         ids=["mha-79-splits", "group4-157-runs", "group3-157-runs", "mha-64-63-splits",
+                              "group4-64-63-runs"])
+def test_decode_merge_of_many_partials(Hq, Hkv, chunk, wgs, S, lens, monkeypatch):
     """Heads with more partials than a wave has lanes (four waves share them,
     each merging 64 at a time with 16 loads in flight): 256-key chunks of a
     20000-key cache (79 splits), and one balanced run per 128-key unit (157
     runs; ragged lengths give 66 and 65; short and empty sequences in the
-    same launch take the one-wave merge)."""
-    B, S, D = 5, 20000, 128
-    lens = [20000, 8321, 8193, 300, 0]
+    same launch take the one-wave merge); and heads with exactly 64 partials
+    (four waves) beside 63 (one wave) and 65."""
+    B, D = len(lens), 128
     if chunk:
         monkeypatch.setenv("ATTN_DECODE_CHUNK", chunk)
     if wgs:
