@@ -237,6 +237,23 @@ def test_decode_balanced_many_batches():
     assert_close(o, ref, torch.bfloat16, "B=300")
 
 
+@pytest.mark.parametrize("d", [128, 256])
+def test_decode_balanced_largest_batch(d):
+    """The balanced pass at its batch limit (2048 sequences: the unit prefix
+    takes 8 batches per thread and 8 KiB of dynamic LDS, beside 128 KiB of
+    staging at d = 256), ragged lengths with empty sequences."""
+    B, Hq, Hkv, S = 2048, 4, 1, 40
+    g = np.random.default_rng(12)
+    lens = [int(x) for x in g.integers(0, S + 1, B)]
+    lens[0], lens[2047] = S, 0
+    say(f"decode balanced B=2048 d={d}")
+    x = make(B, Hq, Hkv, 1, S, d, seed=19)
+    o = attn.decode(x["q"], x["k"], x["v"], kv_lens=lens_tensor(lens))
+    torch.cuda.synchronize()
+    ref = oracle.decode(x["q"].cpu(), x["k"].cpu(), x["v"].cpu(), lens, 1.0 / np.sqrt(d))
+    assert_close(o, ref, torch.bfloat16, f"B=2048 d={d}")
+
+
 MANY_PARTIALS = [
     # Hq, Hkv, forced chunk, forced workgroups, S, lens
     (4, 4, "256", None, 20000, [20000, 8321, 8193, 300, 0]),
