@@ -196,8 +196,52 @@ template <int PER, int ES>
 __device__ __forceinline__ void merge_range(const float* lse, int64_t ls, const float* po, int64_t ps, int nr,
                                             float& M, float& W, float (&acc)[PER]) {
   const int lane = threadIdx.x & 63;
-  M = kNegInf;
-  for (int r = lane; r < nr; r += 64) M = fmaxf(M, lse[(int64_t)r * ls]);
+  // Outputs of partials c + j0 .. c + j0 + kMergeBatch - 1 (up to c + last).
+  auto load_batch = [&](float (&v)[kMergeBatch][PER], int c, int j0, int last) {
+#pragma unroll
+    for (int t = 0; t < kMergeBatch; ++t) {
+#pragma unroll
+      for (int e = 0; e < PER; ++e) v[t][e] = 0.f;
+      if (j0 + t > last) continue;   // uniform across the wave
+      const float* src = po + (int64_t)(c + j0 + t) * ps;
+      if constexpr (ES == 1 && PER == 4) {
+        const float4 x = *reinterpret_cast<const float4*>(src);
+        v[t][0] = x.x; v[t][1] = x.y; v[t][2] = x.z; v[t][3] = x.w;
+      } else if constexpr (ES == 1 && PER == 2) {
+        const float2 x = *reinterpret_cast<const float2*>(src);
+        v[t][0] = x.x; v[t][1] = x.y;
+      } else {
+#pragma unroll
+        for (int e = 0; e < PER; ++e) v[t][e] = src[e * ES];
+      }
+    }
+  };
+  // The first 64 log-sum-exps and the first batch of outputs are loaded
+  // together, before the maximum is known (the outputs do not depend on it),
+  // so a merge of a few partials waits for one round of loads.  The batch's
+  // loads past the last partial re-read it (their weights are 0), which keeps
+  // them free of branches.
+  const float l0 = lane < nr ? lse[(int64_t)lane * ls] : kNegInf;
+  float v0[kMergeBatch][PER];
+  if (nr > 0) {
+    const int last0 = min(kMergeBatch, nr) - 1;
+#pragma unroll
+    for (int t = 0; t < kMergeBatch; ++t) {
+      const float* src = po + (int64_t)min(t, last0) * ps;
+      if constexpr (ES == 1 && PER == 4) {
+        const float4 x = *reinterpret_cast<const float4*>(src);
+        v0[t][0] = x.x; v0[t][1] = x.y; v0[t][2] = x.z; v0[t][3] = x.w;
+      } else if constexpr (ES == 1 && PER == 2) {
+        const float2 x = *reinterpret_cast<const float2*>(src);
+        v0[t][0] = x.x; v0[t][1] = x.y;
+      } else {
+#pragma unroll
+        for (int e = 0; e < PER; ++e) v0[t][e] = src[e * ES];
+      }
+    }
+  }
+  M = l0;
+  for (int r = lane + 64; r < nr; r += 64) M = fmaxf(M, lse[(int64_t)r * ls]);
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, shfl_xor(M, o));
 #pragma unroll
@@ -205,27 +249,19 @@ __device__ __forceinline__ void merge_range(const float* lse, int64_t ls, const 
   W = 0.f;
   for (int c = 0; c < nr; c += 64) {
     const int r = c + lane;
-    const float w = r < nr ? exp2_fast(lse[(int64_t)r * ls] - M) : 0.f;   // weight of partial c + lane
+    const float lr = c == 0 ? l0 : (r < nr ? lse[(int64_t)r * ls] : kNegInf);
+    const float w = r < nr ? exp2_fast(lr - M) : 0.f;   // weight of partial c + lane
     W += w;
     const int last = min(64, nr - c) - 1;
     for (int j0 = 0; j0 <= last; j0 += kMergeBatch) {
       float v[kMergeBatch][PER];
+      if (c == 0 && j0 == 0) {
 #pragma unroll
-      for (int t = 0; t < kMergeBatch; ++t) {
+        for (int t = 0; t < kMergeBatch; ++t)
 #pragma unroll
-        for (int e = 0; e < PER; ++e) v[t][e] = 0.f;
-        if (j0 + t > last) continue;   // uniform across the wave
-        const float* src = po + (int64_t)(c + j0 + t) * ps;
-        if constexpr (ES == 1 && PER == 4) {
-          const float4 x = *reinterpret_cast<const float4*>(src);
-          v[t][0] = x.x; v[t][1] = x.y; v[t][2] = x.z; v[t][3] = x.w;
-        } else if constexpr (ES == 1 && PER == 2) {
-          const float2 x = *reinterpret_cast<const float2*>(src);
-          v[t][0] = x.x; v[t][1] = x.y;
-        } else {
-#pragma unroll
-          for (int e = 0; e < PER; ++e) v[t][e] = src[e * ES];
-        }
+          for (int e = 0; e < PER; ++e) v[t][e] = v0[t][e];
+      } else {
+        load_batch(v, c, j0, last);
       }
 #pragma unroll
       for (int t = 0; t < kMergeBatch; ++t) {
